@@ -1,0 +1,203 @@
+/*
+ * libternary.h -- C ABI of the ternary-weight x int8-activation product on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (BitNet b1.58 inference, I2_S-style storage):
+ *   - weights are ternary, w in {-1, 0, +1}, stored as 2-bit codes
+ *     0, 1, 2 (code = w + 1), four per byte, with one float32 scale per
+ *     tensor stored after the codes ([I2S] "Ternary Representation and
+ *     Packing", "Per-Tensor Scaling Strategy");
+ *   - activations are quantized per token to int8 by absmax ([PARA]
+ *     section 5, Quant8 after the AbsMean / RoundClip equations);
+ *   - the product is an exact integer sum (the +1 / -1 / 0 = add / subtract /
+ *     skip contraction of [PARA] section 5, figure "BitNet b1.58 Ternary
+ *     Matrix Multiplication"), dequantized once by weight scale x activation
+ *     scale / 127 ([I2S] "How I2_S Kernels Process the Format").
+ *
+ * Pages cited:
+ *   [I2S]  "How BitNet's 1-Bit (I2_S) Quantization Works Compared to Standard
+ *          LLM Quantization"
+ *   [PARA] "LLM Quantization Paradigms: FP8, AWQ, EXL2 & BitNet b1.58 in 2026"
+ *   [PREP] "BitNet Inference Preprocessing: Converting Hugging Face
+ *          Checkpoints to I2S GGUF"
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major.  W is [M, K] = [out, in]; x is [N, K]; y is
+ *     [N, M].  N is the number of tokens, 0 <= N <= BT_MAX_N; N = 0 is a
+ *     no-op.
+ *   - Every array argument is a DEVICE pointer, 16-byte aligned, owned by the
+ *     caller.  The library never allocates, frees or synchronizes; scratch
+ *     space is passed in by the caller (bt_layer_io.workspace).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously on it; results are ready when the stream is.
+ *   - Argument errors are returned synchronously as BT_ERR_* and nothing is
+ *     launched.  A failed launch returns BT_ERR_HIP.  A message for the last
+ *     error of the calling thread is in bt_last_error().  Faults inside a
+ *     kernel surface at the caller's next synchronization, as in HIP.
+ *   - Shapes: M % 16 == 0, K % 256 == 0, 0 < K <= 131840 (so that
+ *     |sum| <= 127*K < 2^24 converts to float exactly), M > 0.
+ *   - Results are deterministic: the integer parts (packed bytes, int8
+ *     codes, activation scales, code sums, int32 sums) are exact; float
+ *     outputs do not depend on launch order.
+ */
+#ifndef LIBTERNARY_H
+#define LIBTERNARY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BT_ABI_VERSION 1
+#define BT_MAX_K 131840
+#define BT_MAX_N 2097152 /* tokens per call */
+#define BT_TAIL_BYTES 256
+
+typedef enum {
+    BT_OK = 0,
+    BT_ERR_INVALID_ARG = 1, /* null pointer, negative count, bad enum value */
+    BT_ERR_SHAPE = 2,       /* M % 16, K % 256, K range, mismatched shapes */
+    BT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    BT_ERR_DTYPE = 4,       /* element type not supported for that argument */
+    BT_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
+    BT_ERR_WORKSPACE = 6    /* workspace missing or smaller than required */
+} bt_status;
+
+typedef enum {
+    BT_F32 = 0,   /* IEEE binary32 */
+    BT_BF16 = 1,  /* bfloat16 (top half of a binary32); outputs are rounded
+                     to nearest even from the float32 result */
+    BT_I32 = 2    /* outputs only: the raw int32 sum, no dequantization */
+} bt_dtype;
+
+typedef void *bt_stream; /* hipStream_t */
+
+/* Version of this ABI (BT_ABI_VERSION of the header it was built from). */
+int bt_abi_version(void);
+
+/* Message describing the last error returned on the calling thread
+ * (thread-local, valid until the next call on this thread; "" if none). */
+const char *bt_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Packed ternary weights ([I2S] "Ternary Representation and Packing",
+ * "Per-Tensor Scaling Strategy").
+ *
+ * Byte layout "T16Q256" (the pages fix the code map and the in-byte order,
+ * not the block geometry, which is chosen for 64-lane waves):
+ *   W is cut into tiles of 16 rows x 256 columns; tile (m/16, k/256) is the
+ *   1024 bytes starting at ((m/16)*(K/256) + k/256) * 1024.  Inside a tile,
+ *   slot = (m%16) + 16*((k%64)/16) selects 16 bytes; inside the slot, byte
+ *   4*((k%256)/64) + (k%4); inside the byte, group g = (k%16)/4 occupies
+ *   bits [7-2g : 6-2g] and holds code = W[m,k] + 1.
+ *   So one 16-byte slot read by one lane holds four 32-bit words, each with
+ *   the codes of 16 consecutive columns of one row, and a 64-lane wave
+ *   reading 16 bytes per lane covers one whole tile.
+ *   Bytes [M*K/4, M*K/4+4) hold the float32 scale (little-endian); the
+ *   remaining 252 tail bytes are zero.
+ * ---------------------------------------------------------------------- */
+
+/* Total size in bytes of a packed M x K matrix: M*K/4 + 256.
+ * Returns 0 if the shape is not supported. */
+size_t bt_packed_bytes(int64_t M, int64_t K);
+
+/* Pack w[M][K] (int8, values -1/0/+1) and `scale` into `packed`
+ * (bt_packed_bytes(M, K) bytes).  A value outside {-1,0,+1} is stored as the
+ * nearest state (clamped) and, if `invalid_count` is not NULL, counted: the
+ * kernel ADDS the number of such values to *invalid_count (a device int32 the
+ * caller zeroes beforehand).  Any M, K with M % 16 == 0 and K % 256 == 0. */
+bt_status bt_pack_ternary(const int8_t *w, int64_t M, int64_t K, float scale,
+                          uint8_t *packed, int32_t *invalid_count,
+                          bt_stream stream);
+
+/* Inverse of bt_pack_ternary: w[M][K] = code - 1.  (The scale stays in the
+ * packed tail; read it back with a 4-byte copy from offset M*K/4.) */
+bt_status bt_unpack_ternary(const uint8_t *packed, int64_t M, int64_t K,
+                            int8_t *w, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token absmax int8 activation quantization ([PARA] section 5, Quant8).
+ *   amax[n] = max_k |x[n,k]| (float32; bf16 inputs are widened exactly)
+ *   amax == 0: xq[n,:] = 0, x_scale[n] = 0, x_sum[n] = 0
+ *   else     : inv = 127 / amax (float32 division, correctly rounded)
+ *              xq[n,k] = clamp(round_half_even(x[n,k] * inv), -127, 127)
+ *                        (float32 multiply)
+ *              x_scale[n] = amax,  x_sum[n] = sum_k xq[n,k]
+ * x is [N, K] of x_dtype (BT_F32 or BT_BF16); xq is int8 [N, K]; x_scale is
+ * float32 [N]; x_sum is int32 [N].  Non-finite inputs are outside the
+ * contract.
+ * ---------------------------------------------------------------------- */
+bt_status bt_quant_act(const void *x, bt_dtype x_dtype, int64_t N, int64_t K,
+                       int8_t *xq, float *x_scale, int32_t *x_sum,
+                       bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Ternary matrix product with fused dequantization.
+ *   acc[n,m] = sum_k W[m,k] * xq[n,k]                      (exact int32)
+ *   y[n,m]   = float(acc) * ((s_w * x_scale[n]) / 127)     (float32 ops)
+ * where s_w is the scale stored in the packed tail.  y_dtype BT_F32 / BT_BF16
+ * writes the dequantized value, BT_I32 writes acc.  xq / x_scale / x_sum are
+ * the outputs of bt_quant_act for the same tokens.
+ *
+ * bt_ternary_gemv is the decode path (few tokens: weights are streamed once
+ * from HBM with 128-bit loads, unpacked in registers, and dotted with the
+ * int8 activations, with int8 matrix cores once N is large enough to pay);
+ * bt_ternary_gemm is the prefill path (many tokens: tiled int8 matrix-core
+ * product).  Both accept any N >= 0 and return identical results.
+ * ---------------------------------------------------------------------- */
+bt_status bt_ternary_gemv(const uint8_t *packed, int64_t M, int64_t K,
+                          const int8_t *xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t N,
+                          void *y, bt_dtype y_dtype, bt_stream stream);
+
+bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K,
+                          const int8_t *xq, const float *x_scale,
+                          const int32_t *x_sum, int64_t N,
+                          void *y, bt_dtype y_dtype, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Per-layer projection driver.  One transformer block has seven ternary
+ * projections ([PREP] "Stage 1": q, k, v, o, gate, up, down).  They are run
+ * as four dependent groups that share a quantized input:
+ *   x[0] (attention input)  -> q, k, v      (K[0] == K[1] == K[2])
+ *   x[1] (attention output) -> o            (K[3])
+ *   x[2] (FFN input)        -> gate, up     (K[4] == K[5])
+ *   x[3] (FFN hidden)       -> down         (K[6])
+ * Each group quantizes its input once (bt_quant_act semantics) into the
+ * workspace and runs its projections; the path (decode or prefill) is chosen
+ * from N.  Outputs are identical to calling bt_quant_act followed by
+ * bt_ternary_gemv / bt_ternary_gemm per projection.
+ * ---------------------------------------------------------------------- */
+#define BT_LAYER_PROJ 7
+#define BT_LAYER_INPUTS 4
+
+typedef struct {
+    const uint8_t *w[BT_LAYER_PROJ]; /* packed q,k,v,o,gate,up,down */
+    int64_t M[BT_LAYER_PROJ];
+    int64_t K[BT_LAYER_PROJ];
+} bt_layer;
+
+typedef struct {
+    int64_t N;                          /* tokens */
+    const void *x[BT_LAYER_INPUTS];     /* [N, K of its group], x_dtype */
+    bt_dtype x_dtype;                   /* BT_F32 or BT_BF16 */
+    void *y[BT_LAYER_PROJ];             /* [N, M[p]], y_dtype */
+    bt_dtype y_dtype;                   /* BT_F32, BT_BF16 or BT_I32 */
+    void *workspace;                    /* device scratch, 256-byte aligned */
+    size_t workspace_bytes;             /* >= bt_layer_workspace_bytes() */
+} bt_layer_io;
+
+/* Scratch needed by bt_layer_forward for N tokens (quantized inputs, their
+ * scales and sums).  Returns 0 if the layer's shapes are invalid. */
+size_t bt_layer_workspace_bytes(const bt_layer *layer, int64_t N);
+
+bt_status bt_layer_forward(const bt_layer *layer, const bt_layer_io *io,
+                           bt_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBTERNARY_H */

@@ -1,0 +1,275 @@
+"""Python binding of libternary (ternary-weight x int8-activation product on
+AMD MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libternary.so``.  PyTorch supplies device memory and the current
+stream.  The functions named ``bt_*`` mirror the C ABI in
+``include/libternary.h`` one to one (same names, same argument order; tensors
+are passed as device pointers).  A few helpers below (``pack``,
+``quant_act``, ``gemv``, ``gemm``, ``Layer``) allocate the outputs with
+``torch.empty`` and call them.
+
+If ``libternary.so`` has not been built, importing the binding succeeds but
+every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libternary.so")
+
+BT_OK = 0
+BT_ERR_INVALID_ARG = 1
+BT_ERR_SHAPE = 2
+BT_ERR_ALIGN = 3
+BT_ERR_DTYPE = 4
+BT_ERR_HIP = 5
+BT_ERR_WORKSPACE = 6
+STATUS_NAMES = {0: "BT_OK", 1: "BT_ERR_INVALID_ARG", 2: "BT_ERR_SHAPE",
+                3: "BT_ERR_ALIGN", 4: "BT_ERR_DTYPE", 5: "BT_ERR_HIP",
+                6: "BT_ERR_WORKSPACE"}
+
+BT_F32 = 0
+BT_BF16 = 1
+BT_I32 = 2
+BT_MAX_K = 131840
+BT_LAYER_PROJ = 7
+BT_LAYER_INPUTS = 4
+
+_TORCH_DTYPE = {BT_F32: torch.float32, BT_BF16: torch.bfloat16, BT_I32: torch.int32}
+_BT_DTYPE = {torch.float32: BT_F32, torch.bfloat16: BT_BF16, torch.int32: BT_I32}
+
+
+class BtError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class bt_layer(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p * BT_LAYER_PROJ),
+                ("M", ctypes.c_int64 * BT_LAYER_PROJ),
+                ("K", ctypes.c_int64 * BT_LAYER_PROJ)]
+
+
+class bt_layer_io(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64),
+                ("x", ctypes.c_void_p * BT_LAYER_INPUTS),
+                ("x_dtype", ctypes.c_int),
+                ("y", ctypes.c_void_p * BT_LAYER_PROJ),
+                ("y_dtype", ctypes.c_int),
+                ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libternary.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m ternary_weight_quantized_bt_amd.build` "
+                "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.bt_abi_version.argtypes = []
+        L.bt_abi_version.restype = ctypes.c_int
+        L.bt_last_error.argtypes = []
+        L.bt_last_error.restype = ctypes.c_char_p
+        L.bt_packed_bytes.argtypes = [I64, I64]
+        L.bt_packed_bytes.restype = ctypes.c_size_t
+        L.bt_pack_ternary.argtypes = [P, I64, I64, ctypes.c_float, P, P, P]
+        L.bt_pack_ternary.restype = S
+        L.bt_unpack_ternary.argtypes = [P, I64, I64, P, P]
+        L.bt_unpack_ternary.restype = S
+        L.bt_quant_act.argtypes = [P, S, I64, I64, P, P, P, P]
+        L.bt_quant_act.restype = S
+        for fn in (L.bt_ternary_gemv, L.bt_ternary_gemm):
+            fn.argtypes = [P, I64, I64, P, P, P, I64, P, S, P]
+            fn.restype = S
+        L.bt_layer_workspace_bytes.argtypes = [ctypes.POINTER(bt_layer), I64]
+        L.bt_layer_workspace_bytes.restype = ctypes.c_size_t
+        L.bt_layer_forward.argtypes = [ctypes.POINTER(bt_layer),
+                                       ctypes.POINTER(bt_layer_io), P]
+        L.bt_layer_forward.restype = S
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    """Device pointer of a tensor (or None / a raw integer address)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a tensor, got {type(t)}")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if t.numel() and not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int):
+    if status != BT_OK:
+        raise BtError(status, lib().bt_last_error().decode())
+
+
+# ---------------------------------------------------------------- C ABI ----
+
+def bt_abi_version() -> int:
+    return lib().bt_abi_version()
+
+
+def bt_last_error() -> str:
+    return lib().bt_last_error().decode()
+
+
+def bt_packed_bytes(M: int, K: int) -> int:
+    return lib().bt_packed_bytes(M, K)
+
+
+def bt_pack_ternary(w, M, K, scale, packed, invalid_count=None, stream=None):
+    _check(lib().bt_pack_ternary(_p(w), M, K, float(scale), _p(packed),
+                                 _p(invalid_count), _stream(stream)))
+
+
+def bt_unpack_ternary(packed, M, K, w, stream=None):
+    _check(lib().bt_unpack_ternary(_p(packed), M, K, _p(w), _stream(stream)))
+
+
+def bt_quant_act(x, x_dtype, N, K, xq, x_scale, x_sum, stream=None):
+    _check(lib().bt_quant_act(_p(x), x_dtype, N, K, _p(xq), _p(x_scale),
+                              _p(x_sum), _stream(stream)))
+
+
+def bt_ternary_gemv(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype, stream=None):
+    _check(lib().bt_ternary_gemv(_p(packed), M, K, _p(xq), _p(x_scale), _p(x_sum),
+                                 N, _p(y), y_dtype, _stream(stream)))
+
+
+def bt_ternary_gemm(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype, stream=None):
+    _check(lib().bt_ternary_gemm(_p(packed), M, K, _p(xq), _p(x_scale), _p(x_sum),
+                                 N, _p(y), y_dtype, _stream(stream)))
+
+
+def bt_layer_workspace_bytes(layer: bt_layer, N: int) -> int:
+    return lib().bt_layer_workspace_bytes(ctypes.byref(layer), N)
+
+
+def bt_layer_forward(layer: bt_layer, io: bt_layer_io, stream=None):
+    _check(lib().bt_layer_forward(ctypes.byref(layer), ctypes.byref(io),
+                                  _stream(stream)))
+
+
+# -------------------------------------------------------------- helpers ----
+
+def pack(w: torch.Tensor, scale: float, invalid_count=None, stream=None):
+    """int8 [M, K] device tensor -> packed uint8 device tensor."""
+    M, K = w.shape
+    n = bt_packed_bytes(M, K)
+    if n == 0:
+        raise BtError(BT_ERR_SHAPE, bt_last_error())
+    packed = torch.empty(n, dtype=torch.uint8, device=w.device)
+    bt_pack_ternary(w, M, K, scale, packed, invalid_count, stream)
+    return packed
+
+
+def unpack(packed: torch.Tensor, M: int, K: int, stream=None):
+    w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
+    bt_unpack_ternary(packed, M, K, w, stream)
+    return w
+
+
+def quant_act(x: torch.Tensor, stream=None):
+    """float32 / bfloat16 [N, K] -> (xq int8 [N, K], scale f32 [N], sum i32 [N])."""
+    N, K = x.shape
+    dev = x.device
+    xq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    s = torch.empty(N, dtype=torch.float32, device=dev)
+    sm = torch.empty(N, dtype=torch.int32, device=dev)
+    bt_quant_act(x, _BT_DTYPE[x.dtype], N, K, xq, s, sm, stream)
+    return xq, s, sm
+
+
+def _matmul(fn, packed, M, K, xq, xs, xsum, y_dtype, stream):
+    N = xq.shape[0]
+    y = torch.empty((N, M), dtype=_TORCH_DTYPE[y_dtype], device=xq.device)
+    fn(packed, M, K, xq, xs, xsum, N, y, y_dtype, stream)
+    return y
+
+
+def gemv(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
+    return _matmul(bt_ternary_gemv, packed, M, K, xq, xs, xsum, y_dtype, stream)
+
+
+def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
+    return _matmul(bt_ternary_gemm, packed, M, K, xq, xs, xsum, y_dtype, stream)
+
+
+class Layer:
+    """Seven packed projections (q, k, v, o, gate, up, down) of one block."""
+
+    def __init__(self, packed, shapes):
+        assert len(packed) == BT_LAYER_PROJ and len(shapes) == BT_LAYER_PROJ
+        self.packed = list(packed)  # keeps the tensors alive
+        self.shapes = [tuple(s) for s in shapes]
+        self.c = bt_layer()
+        for p, (t, (M, K)) in enumerate(zip(self.packed, self.shapes)):
+            self.c.w[p] = _p(t)
+            self.c.M[p] = M
+            self.c.K[p] = K
+
+    def workspace_bytes(self, N: int) -> int:
+        return bt_layer_workspace_bytes(self.c, N)
+
+    def make_io(self, xs, ys, y_dtype, workspace) -> bt_layer_io:
+        io = bt_layer_io()
+        io.N = xs[0].shape[0]
+        for i, x in enumerate(xs):
+            io.x[i] = _p(x)
+        io.x_dtype = _BT_DTYPE[xs[0].dtype]
+        for p, y in enumerate(ys):
+            io.y[p] = _p(y)
+        io.y_dtype = y_dtype
+        io.workspace = _p(workspace)
+        io.workspace_bytes = workspace.numel() if workspace is not None else 0
+        return io
+
+    def alloc_outputs(self, N: int, y_dtype: int, device):
+        return [torch.empty((N, M), dtype=_TORCH_DTYPE[y_dtype], device=device)
+                for (M, _) in self.shapes]
+
+    def alloc_workspace(self, N: int, device):
+        # 256-byte alignment: torch's caching allocator returns at least
+        # 512-byte aligned blocks.
+        return torch.empty(max(self.workspace_bytes(N), 256), dtype=torch.uint8,
+                           device=device)
+
+    def forward(self, xs, y_dtype=BT_BF16, ys=None, workspace=None, stream=None):
+        N = xs[0].shape[0]
+        dev = xs[0].device
+        if ys is None:
+            ys = self.alloc_outputs(N, y_dtype, dev)
+        if workspace is None:
+            workspace = self.alloc_workspace(N, dev)
+        io = self.make_io(xs, ys, y_dtype, workspace)
+        bt_layer_forward(self.c, io, stream)
+        return ys

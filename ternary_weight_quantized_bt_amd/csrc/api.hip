@@ -1,0 +1,289 @@
+// api.hip -- the C ABI of libternary: argument validation, dispatch, and the
+// per-layer projection driver.  Host code only; kernels live in the other
+// files.  Nothing here allocates, frees or synchronizes.
+//
+// The seven projections of a block ("BitNet Inference Preprocessing:
+// Converting Hugging Face Checkpoints to I2S GGUF", "Stage 1": q, k, v, o,
+// gate, up, down) are run as four groups that share one quantized input.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bt_status fail(bt_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bt_status ok() {
+    g_err[0] = '\0';
+    return BT_OK;
+}
+
+bt_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(BT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bt_status check_mk(int64_t M, int64_t K, const char *fn) {
+    if (M <= 0 || K <= 0)
+        return fail(BT_ERR_SHAPE, "%s: M and K must be positive (M=%lld, K=%lld)", fn,
+                    (long long)M, (long long)K);
+    if (M % 16 != 0)
+        return fail(BT_ERR_SHAPE, "%s: M=%lld is not a multiple of 16", fn, (long long)M);
+    if (K % 256 != 0)
+        return fail(BT_ERR_SHAPE, "%s: K=%lld is not a multiple of 256", fn, (long long)K);
+    if (K > BT_MAX_K)
+        return fail(BT_ERR_SHAPE, "%s: K=%lld exceeds %d", fn, (long long)K, BT_MAX_K);
+    if (M > (int64_t)1 << 40)
+        return fail(BT_ERR_SHAPE, "%s: M=%lld too large", fn, (long long)M);
+    return BT_OK;
+}
+
+bt_status check_ptr(const void *p, const char *name, const char *fn) {
+    if (p == nullptr) return fail(BT_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+    if (!aligned16(p)) return fail(BT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, name);
+    return BT_OK;
+}
+
+bt_status check_n(int64_t N, const char *fn) {
+    if (N < 0) return fail(BT_ERR_INVALID_ARG, "%s: N=%lld is negative", fn, (long long)N);
+    if (N > BT_MAX_N)
+        return fail(BT_ERR_SHAPE, "%s: N=%lld exceeds %d", fn, (long long)N, BT_MAX_N);
+    return BT_OK;
+}
+
+#define BT_TRY(expr)                        \
+    do {                                    \
+        const bt_status st_ = (expr);       \
+        if (st_ != BT_OK) return st_;       \
+    } while (0)
+
+hipStream_t as_stream(bt_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+bt_status check_matmul(const char *fn, const uint8_t *packed, int64_t M, int64_t K,
+                       const int8_t *xq, const float *xs, const int32_t *xsum,
+                       int64_t N, void *y, bt_dtype ydt) {
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_n(N, fn));
+    if (ydt != BT_F32 && ydt != BT_BF16 && ydt != BT_I32)
+        return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)ydt);
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (N == 0) return BT_OK;
+    BT_TRY(check_ptr(xq, "xq", fn));
+    if (xs == nullptr) return fail(BT_ERR_INVALID_ARG, "%s: x_scale is NULL", fn);
+    if (xsum == nullptr) return fail(BT_ERR_INVALID_ARG, "%s: x_sum is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(xs) & 3u) || (reinterpret_cast<uintptr_t>(xsum) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: x_scale / x_sum not 4-byte aligned", fn);
+    BT_TRY(check_ptr(y, "y", fn));
+    return BT_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace carve-up for a layer: per input i, xq_i [N, K_i], then scales and
+// sums [N] each, every block 256-byte aligned.
+struct LayerWs {
+    int8_t *xq[BT_LAYER_INPUTS];
+    float *xs[BT_LAYER_INPUTS];
+    int32_t *xsum[BT_LAYER_INPUTS];
+    size_t bytes;
+};
+
+bool layer_input_widths(const bt_layer *L, int64_t Kin[BT_LAYER_INPUTS]) {
+    if (L->K[0] != L->K[1] || L->K[0] != L->K[2] || L->K[4] != L->K[5]) return false;
+    Kin[0] = L->K[0];
+    Kin[1] = L->K[3];
+    Kin[2] = L->K[4];
+    Kin[3] = L->K[6];
+    return true;
+}
+
+LayerWs carve(const int64_t Kin[BT_LAYER_INPUTS], int64_t N, void *base) {
+    LayerWs w{};
+    size_t off = 0;
+    uint8_t *b = static_cast<uint8_t *>(base);
+    for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+        w.xq[i] = reinterpret_cast<int8_t *>(b + off);
+        off = align256(off + (size_t)N * (size_t)Kin[i]);
+        w.xs[i] = reinterpret_cast<float *>(b + off);
+        off = align256(off + (size_t)N * sizeof(float));
+        w.xsum[i] = reinterpret_cast<int32_t *>(b + off);
+        off = align256(off + (size_t)N * sizeof(int32_t));
+    }
+    w.bytes = off;
+    return w;
+}
+
+// Token count above which the prefill (tiled matrix-core) kernel is used.
+constexpr int64_t kPrefillMinN = 128;
+
+hipError_t run_group(const bt::Group &g, hipStream_t s) {
+    return g.N >= kPrefillMinN ? bt::launch_prefill(g, s) : bt::launch_decode(g, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bt_abi_version(void) { return BT_ABI_VERSION; }
+
+const char *bt_last_error(void) { return g_err; }
+
+size_t bt_packed_bytes(int64_t M, int64_t K) {
+    if (check_mk(M, K, "bt_packed_bytes") != BT_OK) return 0;
+    ok();
+    return (size_t)(M * K / 4) + BT_TAIL_BYTES;
+}
+
+bt_status bt_pack_ternary(const int8_t *w, int64_t M, int64_t K, float scale,
+                          uint8_t *packed, int32_t *invalid_count, bt_stream stream) {
+    const char *fn = "bt_pack_ternary";
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_ptr(w, "w", fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (invalid_count && (reinterpret_cast<uintptr_t>(invalid_count) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: invalid_count not 4-byte aligned", fn);
+    return hip_status(bt::launch_pack(w, M, K, scale, packed, invalid_count, as_stream(stream)), fn);
+}
+
+bt_status bt_unpack_ternary(const uint8_t *packed, int64_t M, int64_t K, int8_t *w,
+                            bt_stream stream) {
+    const char *fn = "bt_unpack_ternary";
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    BT_TRY(check_ptr(w, "w", fn));
+    return hip_status(bt::launch_unpack(packed, M, K, w, as_stream(stream)), fn);
+}
+
+bt_status bt_quant_act(const void *x, bt_dtype x_dtype, int64_t N, int64_t K, int8_t *xq,
+                       float *x_scale, int32_t *x_sum, bt_stream stream) {
+    const char *fn = "bt_quant_act";
+    BT_TRY(check_n(N, fn));
+    if (x_dtype != BT_F32 && x_dtype != BT_BF16)
+        return fail(BT_ERR_DTYPE, "%s: x dtype must be BT_F32 or BT_BF16", fn);
+    if (K <= 0 || K % 256 != 0 || K > BT_MAX_K)
+        return fail(BT_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 256 <= %d", fn,
+                    (long long)K, BT_MAX_K);
+    if (N == 0) return ok();
+    BT_TRY(check_ptr(x, "x", fn));
+    BT_TRY(check_ptr(xq, "xq", fn));
+    if (x_scale == nullptr || x_sum == nullptr)
+        return fail(BT_ERR_INVALID_ARG, "%s: x_scale / x_sum is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) || (reinterpret_cast<uintptr_t>(x_sum) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: x_scale / x_sum not 4-byte aligned", fn);
+    return hip_status(bt::launch_quant(x, x_dtype, N, K, xq, x_scale, x_sum, as_stream(stream)),
+                      fn);
+}
+
+static bt::Group single_group(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,
+                              const float *xs, const int32_t *xsum, int64_t N, void *y,
+                              bt_dtype ydt) {
+    bt::Group g{};
+    g.p[0] = bt::Proj{packed, M, y};
+    g.count = 1;
+    g.K = K;
+    g.xq = xq;
+    g.xs = xs;
+    g.xsum = xsum;
+    g.N = N;
+    g.ydt = ydt;
+    return g;
+}
+
+bt_status bt_ternary_gemv(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,
+                          const float *x_scale, const int32_t *x_sum, int64_t N, void *y,
+                          bt_dtype y_dtype, bt_stream stream) {
+    const char *fn = "bt_ternary_gemv";
+    BT_TRY(check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, y, y_dtype));
+    if (N == 0) return ok();
+    const bt::Group g = single_group(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype);
+    return hip_status(bt::launch_decode(g, as_stream(stream)), fn);
+}
+
+bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,
+                          const float *x_scale, const int32_t *x_sum, int64_t N, void *y,
+                          bt_dtype y_dtype, bt_stream stream) {
+    const char *fn = "bt_ternary_gemm";
+    BT_TRY(check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, y, y_dtype));
+    if (N == 0) return ok();
+    const bt::Group g = single_group(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype);
+    return hip_status(bt::launch_prefill(g, as_stream(stream)), fn);
+}
+
+size_t bt_layer_workspace_bytes(const bt_layer *L, int64_t N) {
+    if (L == nullptr || N < 0) return 0;
+    int64_t Kin[BT_LAYER_INPUTS];
+    if (!layer_input_widths(L, Kin)) return 0;
+    for (int p = 0; p < BT_LAYER_PROJ; ++p)
+        if (check_mk(L->M[p], L->K[p], "bt_layer_workspace_bytes") != BT_OK) return 0;
+    ok();
+    return carve(Kin, N, nullptr).bytes;
+}
+
+bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream stream) {
+    const char *fn = "bt_layer_forward";
+    if (L == nullptr || io == nullptr)
+        return fail(BT_ERR_INVALID_ARG, "%s: layer or io is NULL", fn);
+    int64_t Kin[BT_LAYER_INPUTS];
+    if (!layer_input_widths(L, Kin))
+        return fail(BT_ERR_SHAPE, "%s: q/k/v (or gate/up) have different K", fn);
+    for (int p = 0; p < BT_LAYER_PROJ; ++p) {
+        BT_TRY(check_mk(L->M[p], L->K[p], fn));
+        BT_TRY(check_ptr(L->w[p], "layer->w[p]", fn));
+    }
+    const int64_t N = io->N;
+    BT_TRY(check_n(N, fn));
+    if (io->x_dtype != BT_F32 && io->x_dtype != BT_BF16)
+        return fail(BT_ERR_DTYPE, "%s: x dtype must be BT_F32 or BT_BF16", fn);
+    if (io->y_dtype != BT_F32 && io->y_dtype != BT_BF16 && io->y_dtype != BT_I32)
+        return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)io->y_dtype);
+    if (N == 0) return ok();
+    for (int i = 0; i < BT_LAYER_INPUTS; ++i) BT_TRY(check_ptr(io->x[i], "io->x[i]", fn));
+    for (int p = 0; p < BT_LAYER_PROJ; ++p) BT_TRY(check_ptr(io->y[p], "io->y[p]", fn));
+    const LayerWs need = carve(Kin, N, nullptr);
+    if (io->workspace == nullptr || io->workspace_bytes < need.bytes)
+        return fail(BT_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need.bytes,
+                    io->workspace == nullptr ? (size_t)0 : io->workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(io->workspace) & 255u)
+        return fail(BT_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+
+    const LayerWs ws = carve(Kin, N, io->workspace);
+    hipStream_t s = as_stream(stream);
+    // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
+    static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
+    static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
+    for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+        hipError_t e = bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i], ws.xs[i],
+                                        ws.xsum[i], s);
+        if (e != hipSuccess) return hip_status(e, fn);
+        bt::Group g{};
+        g.count = kCount[i];
+        for (int j = 0; j < g.count; ++j) {
+            const int p = kFirst[i] + j;
+            g.p[j] = bt::Proj{L->w[p], L->M[p], io->y[p]};
+        }
+        g.K = Kin[i];
+        g.xq = ws.xq[i];
+        g.xs = ws.xs[i];
+        g.xsum = ws.xsum[i];
+        g.N = N;
+        g.ydt = io->y_dtype;
+        e = run_group(g, s);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return ok();
+}
+
+}  // extern "C"

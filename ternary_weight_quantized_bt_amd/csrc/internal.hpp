@@ -1,0 +1,46 @@
+// internal.hpp -- host-side launchers behind the C ABI (validated arguments
+// only; every function enqueues on `s` and returns hipGetLastError()).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "libternary.h"
+
+namespace bt {
+
+hipError_t launch_pack(const int8_t *w, int64_t M, int64_t K, float scale,
+                       uint8_t *packed, int32_t *invalid, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *packed, int64_t M, int64_t K,
+                         int8_t *w, hipStream_t s);
+hipError_t launch_quant(const void *x, bt_dtype xdt, int64_t N, int64_t K,
+                        int8_t *xq, float *xs, int32_t *xsum, hipStream_t s);
+
+// One projection of a grouped launch.
+struct Proj {
+    const uint8_t *packed;
+    int64_t M;
+    void *y;
+};
+constexpr int kMaxGroup = 3;
+struct Group {
+    Proj p[kMaxGroup];
+    int count;
+    int64_t K;                 // shared by every projection of the group
+    const int8_t *xq;          // [N, K]
+    const float *xs;           // [N]
+    const int32_t *xsum;       // [N]
+    int64_t N;
+    bt_dtype ydt;
+};
+
+// Decode path (few tokens): 128-bit weight streaming + dot4, or skinny
+// matrix-core tiles once N is large enough.
+hipError_t launch_decode(const Group &g, hipStream_t s);
+// Prefill path: tiled int8 matrix-core product.
+hipError_t launch_prefill(const Group &g, hipStream_t s);
+
+// Largest N for which launch_decode uses the dot4 kernel.
+constexpr int64_t kDot4MaxN = 4;
+
+}  // namespace bt

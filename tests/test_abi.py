@@ -1,0 +1,166 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (no GPU needed: nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_quantized_bt_amd as bt
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "libternary.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("bt_pack_ternary", "bt_unpack_ternary", "bt_quant_act",
+              "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
+              "bt_layer_workspace_bytes", "bt_packed_bytes", "bt_last_error",
+              "bt_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bt.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert hasattr(bt, name), f"binding lacks {name}"
+
+
+def test_abi_version():
+    assert bt.bt_abi_version() == 1
+
+
+def test_packed_bytes():
+    assert bt.bt_packed_bytes(2560, 2560) == 2560 * 2560 // 4 + 256
+    assert bt.bt_packed_bytes(16, 256) == 16 * 256 // 4 + 256
+    assert bt.bt_packed_bytes(15, 256) == 0
+    assert "multiple of 16" in bt.bt_last_error()
+    assert bt.bt_packed_bytes(16, 200) == 0
+    assert bt.bt_packed_bytes(16, bt.BT_MAX_K + 256) == 0
+
+
+A = 1 << 20  # a fake, 16-byte aligned address: never dereferenced because
+             # validation fails before anything is launched
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 15, 256, 1.0, A, None), bt.BT_ERR_SHAPE),
+    ((A, 16, 300, 1.0, A, None), bt.BT_ERR_SHAPE),
+    ((A, 0, 256, 1.0, A, None), bt.BT_ERR_SHAPE),
+    ((None, 16, 256, 1.0, A, None), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, 1.0, None, None), bt.BT_ERR_INVALID_ARG),
+    ((A + 1, 16, 256, 1.0, A, None), bt.BT_ERR_ALIGN),
+    ((A, 16, 256, 1.0, A, A + 2), bt.BT_ERR_ALIGN),
+])
+def test_pack_validation(args, status):
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_pack_ternary(*args, stream=0)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("fn", ["bt_ternary_gemv", "bt_ternary_gemm"])
+@pytest.mark.parametrize("args,status", [
+    ((A, 16, 256, A, A, A, -1, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, A, A, A, 1, A, 7), bt.BT_ERR_DTYPE),
+    ((A, 16, 256 + 128, A, A, A, 1, A, bt.BT_F32), bt.BT_ERR_SHAPE),
+    ((A, 16, bt.BT_MAX_K + 256, A, A, A, 1, A, bt.BT_F32), bt.BT_ERR_SHAPE),
+    ((A, 16, 256, None, A, A, 1, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, A, None, A, 1, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, A, A, A, 1, A + 8, bt.BT_F32), bt.BT_ERR_ALIGN),
+    ((A + 4, 16, 256, A, A, A, 1, A, bt.BT_F32), bt.BT_ERR_ALIGN),
+])
+def test_matmul_validation(fn, args, status):
+    with pytest.raises(bt.BtError) as e:
+        getattr(bt, fn)(*args, stream=0)
+    assert e.value.status == status
+
+
+def test_matmul_empty_batch_is_a_noop():
+    # N = 0: validated, nothing launched, BT_OK (inputs may be NULL)
+    bt.bt_ternary_gemv(A, 16, 256, None, None, None, 0, None, bt.BT_F32, stream=0)
+    bt.bt_ternary_gemm(A, 16, 256, None, None, None, 0, None, bt.BT_BF16, stream=0)
+    bt.bt_quant_act(None, bt.BT_BF16, 0, 256, None, None, None, stream=0)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, bt.BT_I32, 1, 256, A, A, A), bt.BT_ERR_DTYPE),
+    ((A, bt.BT_F32, 1, 100, A, A, A), bt.BT_ERR_SHAPE),
+    ((A, bt.BT_F32, -3, 256, A, A, A), bt.BT_ERR_INVALID_ARG),
+    ((A + 8, bt.BT_F32, 1, 256, A, A, A), bt.BT_ERR_ALIGN),
+    ((A, bt.BT_F32, 1, 256, A, None, A), bt.BT_ERR_INVALID_ARG),
+])
+def test_quant_validation(args, status):
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_quant_act(*args, stream=0)
+    assert e.value.status == status
+
+
+def _layer(shapes):
+    L = bt.bt_layer()
+    for p, (M, K) in enumerate(shapes):
+        L.w[p] = A
+        L.M[p] = M
+        L.K[p] = K
+    return L
+
+
+LAYER = [(64, 256), (32, 256), (32, 256), (256, 64 * 4), (96, 256), (96, 256),
+         (256, 512)]
+
+
+def test_layer_workspace_bytes():
+    L = _layer(LAYER)
+    n = bt.bt_layer_workspace_bytes(L, 5)
+    # four inputs of widths 256, 256, 256, 512: int8 codes + scales + sums,
+    # each block rounded up to 256 bytes
+    expect = 0
+    for K in (256, 256, 256, 512):
+        expect += -(-5 * K // 256) * 256 + 256 + 256
+    assert n == expect
+    bad = list(LAYER)
+    bad[1] = (32, 512)  # k and q must share K
+    assert bt.bt_layer_workspace_bytes(_layer(bad), 5) == 0
+
+
+def test_layer_validation():
+    L = _layer(LAYER)
+    io = bt.bt_layer_io()
+    io.N = 3
+    for i in range(4):
+        io.x[i] = A
+    for p in range(7):
+        io.y[p] = A
+    io.x_dtype = bt.BT_BF16
+    io.y_dtype = bt.BT_BF16
+    io.workspace = A
+    io.workspace_bytes = 10
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_WORKSPACE
+    io.workspace_bytes = 1 << 20
+    io.x_dtype = bt.BT_I32
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_DTYPE
+    io.x_dtype = bt.BT_F32
+    io.y[6] = None
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_INVALID_ARG
+    io.N = 0  # nothing to do
+    bt.bt_layer_forward(L, io, stream=0)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        bt.bt_ternary_gemv(torch.zeros(16), 16, 256, None, None, None, 0, None,
+                           bt.BT_F32, stream=0)

@@ -1,0 +1,124 @@
+"""Per-layer driver (seven projections in four grouped launches) vs oracle,
+on small layers and on the full-size workloads (all outputs where the oracle
+is quick, seeded samples of output rows otherwise)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ternary_weight_quantized_bt_amd as bt
+import workloads as W
+from parity import (RTOL, as_f64, assert_equal, assert_rel_close,
+                    check_projection, to_np, x_for_oracle)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+YDT = {"f32": bt.BT_F32, "bf16": bt.BT_BF16}
+
+SMALL = W.Workload(
+    name="small_layer", index=9, description="small block with every kind of tail",
+    shapes=((256, 512), (64, 512), (64, 512), (512, 256), (336, 512),
+            (336, 512), (512, 1280)),
+    layers=1, batches=(1, 3, 8, 64, 200), x_dtype="bf16", y_dtype="bf16",
+    weight_dist="p0_0.4", act_dist="normal", outlier_frac=0.01, outlier_scale=20.0)
+
+
+def run_layer(wl, layer, N, ydt, rows_per_proj=None, seed_rows=0):
+    """Build one layer on the GPU, run the driver, compare with the oracle."""
+    ws = W.layer_weights(wl, layer, device="cpu" if wl.layers == 1 else DEV)
+    packed_gpu = [bt.pack(w.to(DEV), s) for (w, s) in ws]
+    L = bt.Layer(packed_gpu, wl.shapes)
+    xs = W.layer_inputs(wl, layer, N, device="cpu")
+    ys = L.forward([x.to(DEV) for x in xs], y_dtype=ydt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed_rows)
+    quant = [oracle.quant_act(x_for_oracle(x)) for x in xs]
+    for p, ((w, s), (M, K)) in enumerate(zip(ws, wl.shapes)):
+        ref_packed, _ = oracle.pack(w.cpu().numpy(), s)
+        assert_equal(to_np(packed_gpu[p]), ref_packed, f"packed {wl.proj_names[p]}")
+        xq, xsc, _ = quant[wl.proj_input[p]]
+        rows = None
+        if rows_per_proj is not None and rows_per_proj < M:
+            rows = np.sort(rng.choice(M, rows_per_proj, replace=False))
+        acc = oracle.matmul_i32(ref_packed, M, K, xq, rows)
+        check_projection(packed_gpu[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt,
+                         rows, f"{wl.name} layer {layer} {wl.proj_names[p]} N={N}")
+    return ys
+
+
+@pytest.mark.parametrize("N", SMALL.batches)
+@pytest.mark.parametrize("ydt", [bt.BT_I32, bt.BT_F32, bt.BT_BF16])
+def test_small_layer(N, ydt):
+    run_layer(SMALL, 0, N, ydt)
+
+
+def test_small_layer_f32_inputs():
+    wl = W.Workload(**{**SMALL.__dict__, "x_dtype": "f32"})
+    run_layer(wl, 0, 5, bt.BT_F32)
+
+
+def test_layer_matches_separate_calls():
+    wl = SMALL
+    N = 17
+    ws = W.layer_weights(wl, 0)
+    packed = [bt.pack(w.to(DEV), s) for (w, s) in ws]
+    L = bt.Layer(packed, wl.shapes)
+    xs = [x.to(DEV) for x in W.layer_inputs(wl, 0, N)]
+    ys = L.forward(xs, y_dtype=bt.BT_BF16)
+    for p, (M, K) in enumerate(wl.shapes):
+        xq, s, sm = bt.quant_act(xs[wl.proj_input[p]])
+        y = bt.gemv(packed[p], M, K, xq, s, sm, bt.BT_BF16)
+        assert torch.equal(y, ys[p])
+
+
+# ------------------------------------------------- full-size workloads ----
+
+def test_workload_gemv_2560():
+    wl = W.GEMV_2560
+    for ydt in (bt.BT_I32, bt.BT_F32):
+        w, s = W.layer_weights(wl, 0)[0]
+        assert s == 0.02
+        M, K = wl.shapes[0]
+        x = W.layer_inputs(wl, 0, 1)[0]
+        packed = bt.pack(w.to(DEV), s)
+        xq, xs, xsum = bt.quant_act(x.to(DEV))
+        y = bt.gemv(packed, M, K, xq, xs, xsum, ydt)
+        ref_packed, _ = oracle.pack(w.numpy(), s)
+        ref = oracle.forward(ref_packed, M, K, x.numpy())
+        assert_equal(to_np(packed), ref_packed, "packed")
+        assert_equal(to_np(xq), ref["xq"], "xq")
+        if ydt == bt.BT_I32:
+            assert_equal(to_np(y), ref["acc"], "acc")
+        else:
+            assert_rel_close(as_f64(y), ref["y"], 1e-6, "y")
+
+
+@pytest.mark.parametrize("ydt", [bt.BT_I32, bt.BT_BF16])
+def test_workload_layer2b_n1(ydt):
+    run_layer(W.LAYER2B_N1, 0, 1, ydt)
+
+
+def test_workload_layer2b_n64():
+    run_layer(W.LAYER2B_N64, 0, 64, bt.BT_BF16)
+    run_layer(W.LAYER2B_N64, 0, 64, bt.BT_I32, rows_per_proj=64)
+
+
+def test_workload_prefill_sampled_rows():
+    run_layer(W.PREFILL2B_N2048, 0, 2048, bt.BT_BF16, rows_per_proj=48, seed_rows=1)
+    run_layer(W.PREFILL2B_N2048, 0, 2048, bt.BT_I32, rows_per_proj=24, seed_rows=2)
+
+
+@pytest.mark.parametrize("layer", [0, 79])
+@pytest.mark.parametrize("N", [1, 8])
+def test_workload_stream70b_sampled_rows(layer, N):
+    run_layer(W.STREAM70B, layer, N, bt.BT_BF16, rows_per_proj=64, seed_rows=layer + N)
+
+
+def test_determinism():
+    outs = [run_layer(SMALL, 0, 64, bt.BT_BF16) for _ in range(3)]
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    for a, b in zip(outs[0], outs[2]):
+        assert torch.equal(a, b)
