@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary-weight x int8-activation hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--tokens N] [--no-graph] [--no-cpu] [--no-extra]
+
+A step is one pass of the whole path over one batch: for every layer, each of
+the four projection groups quantizes its input per token (absmax int8) and
+runs its ternary products with the fused dequantization epilogue.  Weights
+are packed once at load time (not timed; timed separately as "pack").
+Inputs already sit in HBM when the timed region starts.
+
+Default workload: the 80-layer 70B-class weight stream (hidden 8192, FFN
+28672, 64 q / 8 kv heads; 17.1 GB of packed ternary weights) at 1 token.  It
+is the largest single-GPU workload and the only one whose weights cannot sit
+in the 256 MB last-level cache, so its packed-weight GB/s is an HBM figure.
+The same line also reports the 8-token stream and the 2048-token prefill of
+the 2B-class block (int8 TOPS), under "extra".
+
+Prints ONE JSON line (the metric: packed-weight GB/s and fraction of HBM peak
+for decode; int8 TOPS and fraction of the int8 matrix-core peak for prefill).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("packed-weight GB/s & % HBM peak (decode GEMV); "
+          "int8 TOPS & % MFMA peak (prefill)")
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix cores, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("gemv.hip", "mfma.hip", "common.hpp", "group.hpp")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stream70b")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per step (default: the workload's first batch)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="override the number of layers (default: the workload's)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the step eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 8-token stream and the prefill extras")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ternary_weight_quantized_bt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Model:
+    """Packed weights of every layer plus per-step inputs, outputs, workspace."""
+
+    def __init__(self, wl, layers, device):
+        import torch
+        import ternary_weight_quantized_bt_amd as bt
+        import workloads as W
+        self.wl, self.layers, self.device = wl, layers, device
+        self.layer_objs = []
+        t0 = time.perf_counter()
+        pack_s = 0.0
+        for l in range(layers):
+            packed = []
+            for p, (M, K) in enumerate(wl.shapes):
+                w = W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, l, p), device)
+                torch.cuda.synchronize()
+                a = time.perf_counter()
+                packed.append(bt.pack(w, W.weight_scale(wl, p)))
+                torch.cuda.synchronize()
+                pack_s += time.perf_counter() - a
+                del w
+            self.layer_objs.append(bt.Layer(packed, wl.shapes))
+        self.setup_s = time.perf_counter() - t0
+        self.pack_s = pack_s
+        self.packed_bytes = wl.packed_bytes_per_layer * layers
+
+    def set_tokens(self, N):
+        import torch
+        import ternary_weight_quantized_bt_amd as bt
+        import workloads as W
+        wl = self.wl
+        self.N = N
+        ydt = bt.BT_BF16 if wl.y_dtype == "bf16" else bt.BT_F32
+        self.ydt = ydt
+        self.xs = [W.layer_inputs(wl, l, N, self.device) for l in range(self.layers)]
+        L0 = self.layer_objs[0]
+        self.ws = L0.alloc_workspace(N, self.device)
+        self.ys = [L.alloc_outputs(N, ydt, self.device) for L in self.layer_objs]
+        self.ios = [L.make_io(x, y, ydt, self.ws)
+                    for L, x, y in zip(self.layer_objs, self.xs, self.ys)]
+        # quantized copies of every input, for the kernel-only timing pass
+        self.q = [[bt.quant_act(x) for x in xs] for xs in self.xs]
+        self.groups = []
+        first = (0, 3, 4, 6)
+        count = (3, 1, 2, 1)
+        for l, L in enumerate(self.layer_objs):
+            gl = []
+            for i in range(4):
+                items = [(L.packed[p], wl.shapes[p][0], self.ys[l][p])
+                         for p in range(first[i], first[i] + count[i])]
+                gl.append((bt.make_projs(items), count[i], wl.shapes[first[i]][1], i))
+            self.groups.append(gl)
+        torch.cuda.synchronize()
+
+    def step(self):
+        import ternary_weight_quantized_bt_amd as bt
+        for L, io in zip(self.layer_objs, self.ios):
+            bt.bt_layer_forward(L.c, io)
+
+    def products_only(self):
+        """The step's grouped product launches, back to back, on inputs that
+        are already quantized (same kernels and grids as in the step)."""
+        import ternary_weight_quantized_bt_amd as bt
+        for l, gl in enumerate(self.groups):
+            for projs, count, K, i in gl:
+                xq, xs, xsum = self.q[l][i]
+                bt.bt_ternary_matmul_group(projs, count, K, xq, xs, xsum, self.N, self.ydt)
+
+
+def time_region(fn, reps):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall
+
+
+def run_steps(model, steps, warmup, use_graph):
+    """Returns (seconds per step, wall seconds of the timed region)."""
+    import torch
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            model.step()  # eager warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            model.step()
+        fn = g.replay
+    else:
+        fn = model.step
+    for _ in range(warmup):
+        fn()
+    t, wall = time_region(fn, steps)
+    return t / steps, wall
+
+
+def kernel_pass(model, reps):
+    """Average duration of the dominant kernel's launches (HIP events around
+    back-to-back runs of every grouped product of a step)."""
+    model.products_only()
+    t, _ = time_region(model.products_only, reps)
+    launches = 4 * model.layers * reps
+    return t / launches, launches
+
+
+def read_traffic(kernel_name, sha):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_name)
+    if not e or e.get("kernel_sha") != sha:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, N, budget_s):
+    """The oracle on layer 0 of the workload (all seven projections, the same
+    seeded weights and inputs), repeated until the time budget is used."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    dev = "cuda:0"
+    packed = []
+    for p, (M, K) in enumerate(wl.shapes):
+        w = W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, 0, p), dev).cpu().numpy()
+        packed.append(oracle.pack(w, W.weight_scale(wl, p))[0])
+        del w
+    xs = W.layer_inputs(wl, 0, N, dev)
+    xs = [x.cpu().view(torch.uint16).numpy() if x.dtype == torch.bfloat16
+          else x.cpu().numpy() for x in xs]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for p, (M, K) in enumerate(wl.shapes):
+            oracle.forward(packed[p], M, K, xs[wl.proj_input[p]])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    cores = min(cores, len(os.sched_getaffinity(0)))
+    return {
+        "value": round(wl.packed_bytes_per_layer * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"layer 0 of {wl.name} (all 7 projections, {N} token(s)), "
+                  f"{reps} pass(es) in {el:.1f} s",
+    }
+
+
+def prefill_extra(steps, warmup, use_graph):
+    import torch
+    import workloads as W
+    wl = W.PREFILL2B_N2048
+    m = Model(wl, 1, "cuda:0")
+    m.set_tokens(2048)
+    sec, _ = run_steps(m, steps, warmup, use_graph)
+    ops = 2 * 2048 * sum(M * K for M, K in wl.shapes)
+    kt, launches = kernel_pass(m, steps)
+    per_launch_ops = ops / 4
+    res = {
+        "workload": wl.name, "tokens": 2048, "ms_per_step": round(sec * 1e3, 4),
+        "int8_tops": round(ops / sec / 1e12, 2),
+        "frac_of_int8_peak": round(ops / sec / 1e12 / PEAK_INT8_TOPS, 4),
+        "kernel_avg_us": round(kt * 1e6, 2),
+        "kernel_tops": round(per_launch_ops / kt / 1e12, 2),
+    }
+    del m
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import ternary_weight_quantized_bt_amd as bt
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bt.lib()  # fail loudly if the HIP library is missing
+
+    wl = W.BY_NAME[args.workload]
+    layers = args.layers or wl.layers
+    N = args.tokens or wl.batches[0]
+    use_graph = not args.no_graph
+    decode = N < bt.BT_PREFILL_MIN_N
+
+    model = Model(wl, layers, "cuda:0")
+    model.set_tokens(N)
+    print(f"[bench] {wl.name}: {layers} layer(s), {N} token(s), "
+          f"{model.packed_bytes / 1e9:.3f} GB packed, setup {model.setup_s:.1f} s",
+          file=sys.stderr, flush=True)
+
+    sec, wall = run_steps(model, args.steps, args.warmup, use_graph)
+    eager_sec = None
+    if use_graph:
+        eager_sec, _ = run_steps(model, max(3, args.steps // 4), 2, False)
+    kt, launches = kernel_pass(model, max(3, args.steps // 2))
+    sha = kernel_sha()
+    bytes_per_launch = model.packed_bytes / (4 * layers)
+    ops_step = 2 * N * sum(M * K for M, K in wl.shapes) * layers
+    if decode:
+        kernel_name = ("gemv_dot4_kernel" if N <= 4 else "mfma_simple_kernel")
+        value = model.packed_bytes / sec / 1e9
+        unit = "GB/s"
+        achieved = bytes_per_launch / kt / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        kernel_name = "mfma_simple_kernel"
+        value = ops_step / sec / 1e12
+        unit = "TOPS"
+        achieved = ops_step / (4 * layers) / kt / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+    roofline["traffic"] = read_traffic(kernel_name, sha)
+    roofline["kernel"] = kernel_name
+    roofline["kernel_avg_us"] = round(kt * 1e6, 3)
+    roofline["launches_timed"] = launches
+    roofline["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
+
+    extra = {}
+    if not args.no_extra and wl.name == "stream70b" and N == 1:
+        model.set_tokens(8)
+        s8, _ = run_steps(model, args.steps, args.warmup, use_graph)
+        k8, _ = kernel_pass(model, max(3, args.steps // 2))
+        extra["stream70b_8_tokens"] = {
+            "ms_per_step": round(s8 * 1e3, 4),
+            "packed_gb_per_s": round(model.packed_bytes / s8 / 1e9, 2),
+            "frac_of_hbm_peak": round(model.packed_bytes / s8 / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel_avg_us": round(k8 * 1e6, 3),
+            "int8_tops": round(16 * sum(M * K for M, K in wl.shapes) * layers / s8 / 1e12, 2),
+        }
+    packed_bytes_step = model.packed_bytes
+    pack = {"seconds": round(model.pack_s, 3),
+            "int8_weights_gb_per_s": round(4 * packed_bytes_step / model.pack_s / 1e9, 2)}
+    if not args.no_extra:
+        del model
+        torch.cuda.empty_cache()
+        extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, N, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "description": wl.description, "tokens": N,
+            "layers": layers, "projections_per_layer": len(wl.shapes),
+            "packed_bytes_per_step": packed_bytes_step,
+            "int8_ops_per_step": ops_step,
+            "hip_graph": use_graph,
+            "ms_per_step_eager": round(eager_sec * 1e3, 4) if eager_sec else None,
+            "frac_of_hbm_peak" if decode else "frac_of_int8_peak":
+                round(value / (PEAK_HBM_GBS if decode else PEAK_INT8_TOPS), 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "pack_load_time": pack,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

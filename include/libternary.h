@@ -158,6 +158,31 @@ bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K,
                           void *y, bt_dtype y_dtype, bt_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped product: up to BT_MAX_GROUP projections that read the same
+ * quantized input (q/k/v, or gate/up) in one launch, their 16-row tiles laid
+ * end to end in one grid.  This is the GPU form of processing several weight
+ * matrices per invocation to cut launch overhead ([I2S] "How I2_S Kernels
+ * Process the Format", weight-parallel kernels).  All projections share K;
+ * y of projection i is [N, projs[i].M].  The path is chosen from N exactly as
+ * bt_layer_forward does (decode kernels below BT_PREFILL_MIN_N tokens, the
+ * prefill kernel from there on), so results equal per-projection
+ * bt_ternary_gemv / bt_ternary_gemm calls.
+ * ---------------------------------------------------------------------- */
+#define BT_MAX_GROUP 3
+#define BT_PREFILL_MIN_N 128
+
+typedef struct {
+    const uint8_t *packed; /* bt_pack_ternary output, M x K */
+    int64_t M;
+    void *y;               /* [N, M] of y_dtype */
+} bt_proj;
+
+bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
+                                  const int8_t *xq, const float *x_scale,
+                                  const int32_t *x_sum, int64_t N,
+                                  bt_dtype y_dtype, bt_stream stream);
+
+/* ------------------------------------------------------------------------
  * Per-layer projection driver.  One transformer block has seven ternary
  * projections ([PREP] "Stage 1": q, k, v, o, gate, up, down).  They are run
  * as four dependent groups that share a quantized input:
@@ -165,9 +190,11 @@ bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K,
  *   x[1] (attention output) -> o            (K[3])
  *   x[2] (FFN input)        -> gate, up     (K[4] == K[5])
  *   x[3] (FFN hidden)       -> down         (K[6])
- * Each group quantizes its input once (bt_quant_act semantics) into the
- * workspace and runs its projections; the path (decode or prefill) is chosen
- * from N.  Outputs are identical to calling bt_quant_act followed by
+ * Each group quantizes its input once (bt_quant_act semantics) and runs its
+ * projections; the path (decode or prefill) is chosen from N.  For a few
+ * tokens the decode kernel quantizes its input itself (one launch per group);
+ * otherwise the codes go through the workspace, whose contents after the call
+ * are unspecified.  Outputs are identical to calling bt_quant_act followed by
  * bt_ternary_gemv / bt_ternary_gemm per projection.
  * ---------------------------------------------------------------------- */
 #define BT_LAYER_PROJ 7

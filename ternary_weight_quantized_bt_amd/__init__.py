@@ -50,6 +50,16 @@ class BtError(RuntimeError):
         self.status = status
 
 
+BT_MAX_GROUP = 3
+BT_PREFILL_MIN_N = 128
+
+
+class bt_proj(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p),
+                ("M", ctypes.c_int64),
+                ("y", ctypes.c_void_p)]
+
+
 class bt_layer(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p * BT_LAYER_PROJ),
                 ("M", ctypes.c_int64 * BT_LAYER_PROJ),
@@ -95,6 +105,9 @@ def lib() -> ctypes.CDLL:
         for fn in (L.bt_ternary_gemv, L.bt_ternary_gemm):
             fn.argtypes = [P, I64, I64, P, P, P, I64, P, S, P]
             fn.restype = S
+        L.bt_ternary_matmul_group.argtypes = [ctypes.POINTER(bt_proj), S, I64, P, P,
+                                              P, I64, S, P]
+        L.bt_ternary_matmul_group.restype = S
         L.bt_layer_workspace_bytes.argtypes = [ctypes.POINTER(bt_layer), I64]
         L.bt_layer_workspace_bytes.restype = ctypes.c_size_t
         L.bt_layer_forward.argtypes = [ctypes.POINTER(bt_layer),
@@ -168,6 +181,23 @@ def bt_ternary_gemv(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype, stream=None
 def bt_ternary_gemm(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype, stream=None):
     _check(lib().bt_ternary_gemm(_p(packed), M, K, _p(xq), _p(x_scale), _p(x_sum),
                                  N, _p(y), y_dtype, _stream(stream)))
+
+
+def bt_ternary_matmul_group(projs, count, K, xq, x_scale, x_sum, N, y_dtype,
+                            stream=None):
+    """projs: a ctypes array of bt_proj (see make_projs)."""
+    _check(lib().bt_ternary_matmul_group(projs, count, K, _p(xq), _p(x_scale),
+                                         _p(x_sum), N, y_dtype, _stream(stream)))
+
+
+def make_projs(items):
+    """[(packed tensor, M, y tensor), ...] -> ctypes array of bt_proj."""
+    arr = (bt_proj * len(items))()
+    for i, (packed, M, y) in enumerate(items):
+        arr[i].packed = _p(packed)
+        arr[i].M = M
+        arr[i].y = _p(y)
+    return arr
 
 
 def bt_layer_workspace_bytes(layer: bt_layer, N: int) -> int:

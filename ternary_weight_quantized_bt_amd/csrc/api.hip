@@ -126,11 +126,10 @@ LayerWs carve(const int64_t Kin[BT_LAYER_INPUTS], int64_t N, void *base) {
     return w;
 }
 
-// Token count above which the prefill (tiled matrix-core) kernel is used.
-constexpr int64_t kPrefillMinN = 128;
+static_assert(BT_MAX_GROUP == bt::kMaxGroup, "group size");
 
 hipError_t run_group(const bt::Group &g, hipStream_t s) {
-    return g.N >= kPrefillMinN ? bt::launch_prefill(g, s) : bt::launch_decode(g, s);
+    return g.N >= BT_PREFILL_MIN_N ? bt::launch_prefill(g, s) : bt::launch_decode(g, s);
 }
 
 }  // namespace
@@ -222,6 +221,29 @@ bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K, const int
     return hip_status(bt::launch_prefill(g, as_stream(stream)), fn);
 }
 
+bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
+                                  const int8_t *xq, const float *x_scale,
+                                  const int32_t *x_sum, int64_t N, bt_dtype y_dtype,
+                                  bt_stream stream) {
+    const char *fn = "bt_ternary_matmul_group";
+    if (projs == nullptr || count < 1 || count > BT_MAX_GROUP)
+        return fail(BT_ERR_INVALID_ARG, "%s: need 1..%d projections", fn, BT_MAX_GROUP);
+    for (int i = 0; i < count; ++i)
+        BT_TRY(check_matmul(fn, projs[i].packed, projs[i].M, K, xq, x_scale, x_sum, N,
+                            projs[i].y, y_dtype));
+    if (N == 0) return ok();
+    bt::Group g{};
+    g.count = count;
+    for (int i = 0; i < count; ++i) g.p[i] = bt::Proj{projs[i].packed, projs[i].M, projs[i].y};
+    g.K = K;
+    g.xq = xq;
+    g.xs = x_scale;
+    g.xsum = x_sum;
+    g.N = N;
+    g.ydt = y_dtype;
+    return hip_status(run_group(g, as_stream(stream)), fn);
+}
+
 size_t bt_layer_workspace_bytes(const bt_layer *L, int64_t N) {
     if (L == nullptr || N < 0) return 0;
     int64_t Kin[BT_LAYER_INPUTS];
@@ -265,9 +287,6 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
     static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
     static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
-        hipError_t e = bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i], ws.xs[i],
-                                        ws.xsum[i], s);
-        if (e != hipSuccess) return hip_status(e, fn);
         bt::Group g{};
         g.count = kCount[i];
         for (int j = 0; j < g.count; ++j) {
@@ -280,7 +299,15 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         g.xsum = ws.xsum[i];
         g.N = N;
         g.ydt = io->y_dtype;
-        e = run_group(g, s);
+        hipError_t e;
+        if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, Kin[i], io->x_dtype)) {
+            // one launch: the decode kernel quantizes its input itself
+            e = bt::launch_decode_fused(g, io->x[i], io->x_dtype, s);
+        } else {
+            e = bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i], ws.xs[i],
+                                 ws.xsum[i], s);
+            if (e == hipSuccess) e = run_group(g, s);
+        }
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();

@@ -14,7 +14,19 @@
 namespace bt {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Pointers into global memory.  Loads through them compile to global_load
+// (counted by vmcnt only) rather than flat_load, whose lgkmcnt side would make
+// every LDS wait also drain the in-flight HBM loads.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T *p) {
+    return (gptr<T>)p;
+}
 
 constexpr int kWave = 64;
 constexpr int kTileRows = 16;     // rows of one packed tile
@@ -54,19 +66,19 @@ __device__ __forceinline__ float token_factor(float s_w, float s_a) {
 __device__ __forceinline__ void store_out(void *y, int ydt, int64_t idx,
                                           int32_t acc, float factor) {
     if (ydt == BT_I32) {
-        reinterpret_cast<int32_t *>(y)[idx] = acc;
+        to_global(reinterpret_cast<int32_t *>(y))[idx] = acc;
     } else {
         float v = __fmul_rn((float)acc, factor);
         if (ydt == BT_F32)
-            reinterpret_cast<float *>(y)[idx] = v;
+            to_global(reinterpret_cast<float *>(y))[idx] = v;
         else
-            reinterpret_cast<uint16_t *>(y)[idx] = f32_to_bf16(v);
+            to_global(reinterpret_cast<uint16_t *>(y))[idx] = f32_to_bf16(v);
     }
 }
 
 __device__ __forceinline__ float packed_scale(const uint8_t *packed,
                                               int64_t M, int64_t K) {
-    return *reinterpret_cast<const float *>(packed + M * K / 4);
+    return *to_global(reinterpret_cast<const float *>(packed + M * K / 4));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {

@@ -54,6 +54,7 @@ struct TileRef {
     void *y;
     int64_t M;
     int64_t mt;
+    int proj;  // index of the projection within the group
 };
 
 // Branch-free pick among three loaded values with all-ones / all-zeros masks.
@@ -62,6 +63,15 @@ struct TileRef {
 __device__ __forceinline__ uint64_t pick3(uint64_t m1, uint64_t m2, uint64_t v0,
                                           uint64_t v1, uint64_t v2) {
     return (v0 & ~m1) | (v1 & m1 & ~m2) | (v2 & m2);
+}
+
+// Weight scale of projection p of the group (read from its packed tail).
+__device__ __forceinline__ float group_weight_scale(const GroupArgs &a, int p) {
+    const uint64_t m1 = p >= 1 ? ~0ull : 0ull, m2 = p >= 2 ? ~0ull : 0ull;
+    const uint8_t *packed = reinterpret_cast<const uint8_t *>(
+        pick3(m1, m2, (uint64_t)a.packed[0], (uint64_t)a.packed[1], (uint64_t)a.packed[2]));
+    const int64_t M = (int64_t)pick3(m1, m2, (uint64_t)a.M[0], (uint64_t)a.M[1], (uint64_t)a.M[2]);
+    return packed_scale(packed, M, a.K);
 }
 
 __device__ __forceinline__ TileRef resolve_tile(const GroupArgs &a, int64_t tile) {
@@ -75,6 +85,7 @@ __device__ __forceinline__ TileRef resolve_tile(const GroupArgs &a, int64_t tile
     t.M = (int64_t)pick3(m1, m2, (uint64_t)a.M[0], (uint64_t)a.M[1], (uint64_t)a.M[2]);
     t.mt = tile - (int64_t)pick3(m1, m2, 0ull, (uint64_t)a.tiles_end[0],
                                  (uint64_t)a.tiles_end[1]);
+    t.proj = (int)(m1 & 1u) + (int)(m2 & 1u);
     return t;
 }
 

@@ -37,6 +37,11 @@ struct Group {
 // Decode path (few tokens): 128-bit weight streaming + dot4, or skinny
 // matrix-core tiles once N is large enough.
 hipError_t launch_decode(const Group &g, hipStream_t s);
+// Decode path with the activation quantization fused into the kernel's
+// prologue (x is the float / bf16 input of the group).  Only for shapes where
+// decode_fuses_quant(N, K) holds.
+bool decode_fuses_quant(int64_t N, int64_t K, bt_dtype xdt);
+hipError_t launch_decode_fused(const Group &g, const void *x, bt_dtype xdt, hipStream_t s);
 // Prefill path: tiled int8 matrix-core product.
 hipError_t launch_prefill(const Group &g, hipStream_t s);
 

@@ -44,14 +44,14 @@ void mfma_simple_kernel(GroupArgs a) {
     const int64_t K = a.K, qb = K / kTileCols;
     const int r = lane % 16, h = lane / 16;
     const int64_t nb = (int64_t)blockIdx.y * 16 * TG;
-    const uint4 *wp = reinterpret_cast<const uint4 *>(tr.packed + tr.mt * qb * kTileBytes) + lane;
+    gptr<const v4u> wp = to_global(reinterpret_cast<const v4u *>(tr.packed + tr.mt * qb * kTileBytes)) + lane;
 
     v4i acc[TG];
 #pragma unroll
     for (int g = 0; g < TG; ++g) acc[g] = v4i{0, 0, 0, 0};
 
     for (int64_t q = 0; q < qb; ++q) {
-        const uint4 p = wp[q * kWave];
+        const v4u p = wp[q * kWave];
         const uint32_t words[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {

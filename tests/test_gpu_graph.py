@@ -1,0 +1,56 @@
+"""The layer driver captured in a HIP graph: every replay, with eager work and
+synchronizations between replays, equals the eager result.  (No kernel of the
+library records a memset, so the step is capturable.)"""
+import pytest
+import torch
+
+import ternary_weight_quantized_bt_amd as bt
+import workloads as W
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("N", [1, 8, 200])
+def test_graph_replays_match_eager(N):
+    wl = W.LAYER2B_N1
+    layers = []
+    for l in range(2):
+        packed = [bt.pack(w.to(DEV), s) for w, s in W.layer_weights(wl, l)]
+        layers.append(bt.Layer(packed, wl.shapes))
+    xs = [[x.to(DEV) for x in W.layer_inputs(wl, l, N)] for l in range(2)]
+    ws = layers[0].alloc_workspace(N, DEV)
+    ys = [L.alloc_outputs(N, bt.BT_BF16, DEV) for L in layers]
+    ios = [L.make_io(x, y, bt.BT_BF16, ws) for L, x, y in zip(layers, xs, ys)]
+
+    def step():
+        for L, io in zip(layers, ios):
+            bt.bt_layer_forward(L.c, io)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [[y.clone() for y in yl] for yl in ys]
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for yl in ys:
+            for y in yl:
+                y.fill_(0)           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for yl, el in zip(ys, eager):
+            for y, e in zip(yl, el):
+                assert torch.equal(y, e), f"replay {rep} differs"
+        step()                       # eager launch between replays
+        torch.cuda.synchronize()
