@@ -76,6 +76,30 @@ __device__ __forceinline__ void store_out(void *y, int ydt, int64_t idx,
     }
 }
 
+// Store four consecutive outputs y[idx .. idx+3] (idx a multiple of 4) with
+// one vector store: acc[v] - sub, dequantized by `factor` unless BT_I32.
+__device__ __forceinline__ void store_out4(void *y, int ydt, int64_t idx, const v4i acc,
+                                           int32_t sub, float factor) {
+    if (ydt == BT_I32) {
+        *to_global(reinterpret_cast<v4i *>(reinterpret_cast<int32_t *>(y) + idx)) =
+            v4i{acc.x - sub, acc.y - sub, acc.z - sub, acc.w - sub};
+        return;
+    }
+    const float v0 = __fmul_rn((float)(acc.x - sub), factor);
+    const float v1 = __fmul_rn((float)(acc.y - sub), factor);
+    const float v2 = __fmul_rn((float)(acc.z - sub), factor);
+    const float v3 = __fmul_rn((float)(acc.w - sub), factor);
+    if (ydt == BT_F32) {
+        *to_global(reinterpret_cast<v4u *>(reinterpret_cast<float *>(y) + idx)) =
+            v4u{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)};
+    } else {
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        *to_global(reinterpret_cast<v2u *>(reinterpret_cast<uint16_t *>(y) + idx)) =
+            v2u{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+    }
+}
+
 __device__ __forceinline__ float packed_scale(const uint8_t *packed,
                                               int64_t M, int64_t K) {
     return *to_global(reinterpret_cast<const float *>(packed + M * K / 4));

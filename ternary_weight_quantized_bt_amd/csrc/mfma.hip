@@ -98,9 +98,5 @@ hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     return launch_simple<4, 4>(a, s);
 }
 
-hipError_t launch_prefill(const Group &g, hipStream_t s) {
-    if (g.N == 0) return hipSuccess;
-    return launch_simple<4, 4>(make_group_args(g), s);
-}
 
 }  // namespace bt

@@ -1,0 +1,238 @@
+// prefill.hip -- tiled int8 matrix-core product for many tokens (prefill).
+//
+// The ternary contraction ([PARA] section 5, figure "BitNet b1.58 Ternary
+// Matrix Multiplication") is a dense int8 contraction once the codes 0/1/2
+// ([I2S] "Ternary Representation and Packing") are unpacked:
+//   acc[n,m] = sum_k code[m,k] * xq[n,k] - xsum[n]
+// so it runs on v_mfma_i32_16x16x64_i8 with an exact int32 accumulate.
+//
+// Work decomposition.  A workgroup computes a BM x BN output tile (BM rows of
+// the grouped projections, BN tokens) with WMW x WNW waves; a wave owns
+// RT row tiles x TG token groups of 16 x 16.  The K loop walks 256-column
+// blocks:
+//   * A (weights): every lane loads its 16-byte packed slot of each of its RT
+//     row tiles straight into registers (T16Q256: word t of the slot is the
+//     16 codes of row lane%16, columns 64*t + 16*(lane/16) + 0..15), and one
+//     word unpacks with shifts and masks into the lane's A operand of one
+//     16x16x64 instruction.  Weights never touch LDS.
+//   * B (activations): the BN x 256 int8 block is copied global -> LDS with
+//     the direct 16-byte LDS-load instruction (no registers), double
+//     buffered, the next block in flight while the current one is consumed.
+//     Inside a token's 256-byte row, 16-byte chunk c is stored at position
+//     c ^ (token % 16), so the 16 lanes that read one chunk of 16 different
+//     tokens hit 16 different bank groups.
+//   * After the last block the epilogue subtracts the token's code sum and
+//     dequantizes (float32: acc * (s_w * s_a / 127)) to fp32 / bf16, or
+//     writes the int32 sum.
+// The tile order is XCD-aware: workgroups are handed to the eight XCDs
+// round-robin, so workgroup i is mapped to tile (i % 8) * ceil(T / 8) + i / 8
+// of the token-major tile list -- each XCD then works through a contiguous
+// run of tiles that share activation rows, which stay in its L2.
+
+#include "group.hpp"
+
+namespace bt {
+
+namespace {
+
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ v4i unpack_a(uint32_t word) {
+    v4i a;
+    a.x = (int)codes_of_group(word, 0);
+    a.y = (int)codes_of_group(word, 1);
+    a.z = (int)codes_of_group(word, 2);
+    a.w = (int)codes_of_group(word, 3);
+    return a;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int RT, int TG, int WMW, int WNW, int S>
+__global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(GroupArgs a, int64_t mtiles) {
+    constexpr int kWaves = WMW * WNW;
+    constexpr int BN = 16 * TG * WNW;       // tokens per workgroup tile
+    constexpr int BMT = RT * WMW;           // row tiles per workgroup tile
+    constexpr int kRow = kTileCols;         // bytes of one token row of a block
+    constexpr int kDma = BN * kRow / 1024;  // 1 KiB direct loads per block
+    static_assert(kDma % kWaves == 0, "direct loads must split evenly over the waves");
+    constexpr int kDmaW = kDma / kWaves;    // per wave and block
+    constexpr int kVm = RT + kDmaW;         // vector-memory operations per wave and block
+    static_assert((S - 2) * kVm <= 63, "wait count exceeds the counter");
+    // One LDS object per stage (not one array): the compiler can then see that
+    // a direct load into one stage does not alias reads of another, and need
+    // not drain every outstanding load before each barrier.
+    __shared__ __attribute__((aligned(1024))) int8_t sB0[BN * kRow];
+    __shared__ __attribute__((aligned(1024))) int8_t sB1[BN * kRow];
+    __shared__ __attribute__((aligned(1024))) int8_t sB2[S > 2 ? BN * kRow : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sB3[S > 3 ? BN * kRow : 16];
+    static_assert(S >= 2 && S <= 4, "two to four stages");
+    auto stage = [&](int st) -> int8_t * {
+        return st == 0 ? sB0 : (st == 1 ? sB1 : (st == 2 ? sB2 : sB3));
+    };
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int r = lane % 16, h = lane / 16;
+    const int64_t K = a.K, qb = K / kTileCols, N = a.N;
+    const int64_t total = group_tiles(a);  // 16-row tiles of the group
+
+    // XCD-aware tile order (see the header).
+    const int64_t ntok = (N + BN - 1) / BN;
+    const int64_t ntiles = mtiles * ntok;
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    const int64_t idx = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (idx >= ntiles) return;  // whole workgroup
+    const int64_t tn = idx / mtiles, tm = idx % mtiles;
+    const int64_t tok0 = tn * BN;
+
+    // This wave's row tiles (clamped to the last tile past the end; their
+    // results are not stored): wave-uniform base addresses plus the lane's
+    // 16-byte offset at each load.
+    const uint8_t *abase[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
+        abase[i] = tr.packed + tr.mt * qb * kTileBytes;
+    }
+
+    // All loads of block q (clamped to the last block, so every call issues
+    // exactly kVm operations and the wait counts below stay exact): the A
+    // slots into registers, the token block into LDS stage st.  Each 1 KiB
+    // direct load covers 4 tokens; lane l fills position l%16 of token l/16
+    // with global chunk (l%16) ^ (token % 16).
+    v4u ar[S][RT];
+    auto issue = [&](int64_t q, int st) {
+        q = min(q, qb - 1);
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+            ar[st][i] = *to_global(reinterpret_cast<const v4u *>(abase[i] + q * kTileBytes) + lane);
+#pragma unroll
+        for (int i = 0; i < kDmaW; ++i) {
+            const int d = wave * kDmaW + i;   // 1 KiB unit of the block
+            const int tl = d * 4 + lane / 16;  // token within the tile
+            const int64_t tok = min(tok0 + tl, N - 1);
+            const int c = (lane % 16) ^ (tl % 16);
+            const int8_t *src = a.xq + tok * K + q * kTileCols + 16 * c;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(stage(st) + d * 1024), 16, 0, 0);
+        }
+    };
+    // B fragment of token group g, 64-column step t, from stage st: token
+    // g*16 + r of this wave, chunk 4t + h, stored at (4t + h) ^ (token % 16).
+    auto read_b = [&](int st, int t, int g) {
+        return *reinterpret_cast<const v4i *>(stage(st) + (wn * 16 * TG + g * 16 + r) * kRow +
+                                              16 * ((4 * t + h) ^ r));
+    };
+
+    v4i acc[RT][TG];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int g = 0; g < TG; ++g) acc[i][g] = v4i{0, 0, 0, 0};
+
+    // Prologue: blocks 0 .. S-2 in flight.
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue(s, s);
+
+    // Block q: wait until it has landed for every wave (S-2 younger blocks
+    // may stay in flight), barrier -- which also means every wave is done
+    // with block q-1 -- then refill that block's stage with block q+S-1 and
+    // compute block q.  Unrolled by S so stages and registers are static.
+    for (int64_t q0 = 0; q0 < qb; q0 += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int64_t q = q0 + s;
+            if (q >= qb) break;  // uniform
+            // Block q's direct loads are complete for this wave once at most
+            // the S-2 younger blocks are outstanding; the bare barrier (no
+            // fence: a fence would drain those younger loads too) then makes
+            // every wave's part of the block visible.
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * kVm));
+            __builtin_amdgcn_s_barrier();
+            issue(q + S - 1, (s + S - 1) % S);
+            v4i bcur[TG], bnext[TG];
+#pragma unroll
+            for (int g = 0; g < TG; ++g) bcur[g] = read_b(s, 0, g);
+            // The next step's fragments are read while this step's matrix
+            // instructions run; a scheduling fence per step keeps the
+            // scheduler from hoisting every step's operands at once.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (t < 3) {
+#pragma unroll
+                    for (int g = 0; g < TG; ++g) bnext[g] = read_b(s, t + 1, g);
+                }
+                v4i A[RT];
+#pragma unroll
+                for (int i = 0; i < RT; ++i) A[i] = unpack_a(ar[s][i][t]);
+#pragma unroll
+                for (int g = 0; g < TG; ++g)
+#pragma unroll
+                    for (int i = 0; i < RT; ++i)
+                        acc[i][g] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], bcur[g], acc[i][g], 0, 0, 0);
+                if (t < 3) {
+#pragma unroll
+                    for (int g = 0; g < TG; ++g) bcur[g] = bnext[g];
+                }
+            }
+        }
+    }
+
+    // Epilogue: lane (r, h) holds rows 4h..4h+3 of each row tile for token
+    // g*16 + r of each group.  Per-row-tile values are wave-uniform; token
+    // values are loaded from a clamped index so only the stores branch.
+    float s_w[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
+        s_w[i] = packed_scale(tr.packed, tr.M, K);
+    }
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+        const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;
+        const int64_t tc = min(tok, N - 1);
+        const float s_a = a.xs[tc];
+        const int32_t sub = a.xsum[tc];
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const int64_t t = tm * BMT + wm * RT + i;
+            if (t >= total) continue;  // uniform
+            const TileRef tr = resolve_tile(a, t);
+            const float f = token_factor(s_w[i], s_a);
+            const int64_t base = tok * tr.M + tr.mt * kTileRows + 4 * h;
+            if (tok < N) store_out4(tr.y, a.ydt, base, acc[i][g], sub, f);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep one token group's values live at a time
+    }
+}
+
+template <int RT, int TG, int WMW, int WNW, int S>
+hipError_t launch_tiles(const GroupArgs &a, hipStream_t s) {
+    constexpr int BMT = RT * WMW, BN = 16 * TG * WNW;
+    const int64_t mtiles = (group_tiles(a) + BMT - 1) / BMT;
+    const int64_t ntiles = mtiles * ((a.N + BN - 1) / BN);
+    const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((prefill_kernel<RT, TG, WMW, WNW, S>), dim3((unsigned)grid),
+                       dim3(WMW * WNW * kWave), 0, s, a, mtiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const Group &g, hipStream_t s) {
+    if (g.N == 0) return hipSuccess;
+    const GroupArgs a = make_group_args(g);
+    // 256 rows x 64 tokens per workgroup (4 waves of 64 x 64), 3 stages of
+    // 16 KiB: two workgroups per CU.
+    return launch_tiles<4, 4, 4, 1, 3>(a, s);
+}
+
+}  // namespace bt
