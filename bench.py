@@ -37,7 +37,14 @@ METRIC = ("packed-weight GB/s & % HBM peak (decode GEMV); "
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix cores, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("gemv.hip", "mfma.hip", "common.hpp", "group.hpp")
+# Sources of each measured kernel: a traffic record is only used while they
+# are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "decode_dot4_kernel (fused quantization)": ("gemv.hip", "common.hpp", "group.hpp", "quant.hpp"),
+    "decode_dot4_kernel": ("gemv.hip", "common.hpp", "group.hpp", "quant.hpp"),
+    "mfma_decode_kernel": ("mfma.hip", "common.hpp", "group.hpp"),
+    "prefill_kernel": ("prefill.hip", "common.hpp", "group.hpp"),
+}
 
 
 def parse():
@@ -56,12 +63,15 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 8-token stream and the prefill extras")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device-to-device copy of 1 GiB, five times "
+                         "(reference for the HBM traffic counters)")
     return ap.parse_args()
 
 
-def kernel_sha() -> str:
+def kernel_sha(kernel_name: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel_name]:
         with open(os.path.join(ROOT, "ternary_weight_quantized_bt_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -267,6 +277,16 @@ def main():
         sys.exit(2)
     bt.lib()  # fail loudly if the HIP library is missing
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 5}))
+        return
+
     wl = W.BY_NAME[args.workload]
     layers = args.layers or wl.layers
     N = args.tokens or wl.batches[0]
@@ -283,29 +303,44 @@ def main():
     eager_sec = None
     if use_graph:
         eager_sec, _ = run_steps(model, max(3, args.steps // 4), 2, False)
+    # Grouped products alone, on inputs quantized beforehand (same kernels and
+    # grids as the step, minus the fused quantization of the decode path).
     kt, launches = kernel_pass(model, max(3, args.steps // 2))
-    sha = kernel_sha()
-    bytes_per_launch = model.packed_bytes / (4 * layers)
+    launches_per_step = 4 * layers
+    bytes_per_launch = model.packed_bytes / launches_per_step
     ops_step = 2 * N * sum(M * K for M, K in wl.shapes) * layers
+    fused = N <= 4 and all(n * k <= 65536 for k in wl.input_widths()
+                           for n in [1 if N == 1 else (2 if N == 2 else 4)])
     if decode:
-        kernel_name = ("gemv_dot4_kernel" if N <= 4 else "mfma_simple_kernel")
         value = model.packed_bytes / sec / 1e9
         unit = "GB/s"
-        achieved = bytes_per_launch / kt / 1e9
+        if fused:
+            # The step consists of nothing but these launches (the
+            # quantization is fused into them), so their average duration is
+            # the step time over the launch count, from the HIP events around
+            # the timed region.
+            kernel_name = "decode_dot4_kernel (fused quantization)"
+            kavg = sec / launches_per_step
+        else:
+            kernel_name = "decode_dot4_kernel" if N <= 4 else "mfma_decode_kernel"
+            kavg = kt
+        achieved = bytes_per_launch / kavg / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
-        kernel_name = "mfma_simple_kernel"
+        kernel_name = "prefill_kernel"
+        kavg = kt
         value = ops_step / sec / 1e12
         unit = "TOPS"
-        achieved = ops_step / (4 * layers) / kt / 1e12
+        achieved = ops_step / launches_per_step / kavg / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-    roofline["traffic"] = read_traffic(kernel_name, sha)
+    roofline["traffic"] = read_traffic(kernel_name, kernel_sha(kernel_name))
     roofline["kernel"] = kernel_name
-    roofline["kernel_avg_us"] = round(kt * 1e6, 3)
-    roofline["launches_timed"] = launches
+    roofline["kernel_avg_us"] = round(kavg * 1e6, 3)
+    roofline["launches_per_step"] = launches_per_step
     roofline["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
+    roofline["prequantized_kernel_avg_us"] = round(kt * 1e6, 3)
 
     extra = {}
     if not args.no_extra and wl.name == "stream70b" and N == 1:
