@@ -364,20 +364,6 @@ void decode_dot4_kernel(GroupArgs a, DecodeX dx) {
     }
 }
 
-int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
 int tokens_per_pass(int64_t N) { return N == 1 ? 1 : (N == 2 ? 2 : 4); }
 
 // Whether the fused prologue can hold the raw input of every token.
@@ -418,6 +404,20 @@ hipError_t launch_dec_any(const GroupArgs &a, const DecodeX &dx, int mode, bt_dt
 }
 
 }  // namespace
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s);
 

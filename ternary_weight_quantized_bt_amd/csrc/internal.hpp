@@ -45,6 +45,9 @@ hipError_t launch_decode_fused(const Group &g, const void *x, bt_dtype xdt, hipS
 // Prefill path: tiled int8 matrix-core product.
 hipError_t launch_prefill(const Group &g, hipStream_t s);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 // Largest N for which launch_decode uses the dot4 kernel.
 constexpr int64_t kDot4MaxN = 4;
 

@@ -1,10 +1,14 @@
-// mfma.hip -- int8 matrix-core product for more than a handful of tokens.
+// mfma.hip -- batched decode: a few to a hundred tokens per weight pass, on
+// the int8 matrix cores.
 //
 // The ternary contraction ([PARA] section 5, figure "BitNet b1.58 Ternary
 // Matrix Multiplication") is a dense int8 contraction once the codes
-// 0/1/2 ([I2S] "Ternary Representation and Packing") are unpacked, so it runs
-// on v_mfma_i32_16x16x64_i8: acc = sum code*xq over 64 columns per
-// instruction, minus the token's code sum at the end.
+// 0/1/2 ([I2S] "Ternary Representation and Packing") are unpacked, so each
+// 64-column step runs on one v_mfma_i32_16x16x64_i8 (16 rows x 16 tokens):
+// acc = sum code*xq, minus the token's code sum at the end.  The weights are
+// unpacked once per fragment and reused by all 16 tokens of the instruction
+// (the GPU form of the pages' activation-parallel kernel, [I2S] "How I2_S
+// Kernels Process the Format").
 //
 // Operand mapping.  A 16-byte packed slot of lane l holds, in word t, the
 // codes of row l%16 at columns 64*t + 16*(l/16) + 0..15; unpacking one word
@@ -14,13 +18,39 @@
 // Because A and B of a lane then cover the same columns in the same byte
 // order, the instruction sums over exactly those 64 columns whatever order
 // the hardware gives the lane groups.  The 16x16 result lands as: lane l,
-// register v = row 4*(l/16) + v, token l%16.
+// register v = row 4*(l/16) + v, token l%16 -- four consecutive outputs of
+// one token, stored with one vector store.
+//
+// Schedule (the weight stream is the bound: 8 bytes of weights per 4x16
+// multiply-adds).  Persistent grid, one 16-token group per workgroup
+// (gridDim.y groups for more tokens).  The workgroup stages its tokens' codes
+// once, global -> LDS with direct 16-byte loads, and then walks the 16-row
+// tiles of the group with a stride of the grid size; within a tile its waves
+// split K into contiguous runs of 256-column blocks, and each wave keeps RING
+// weight-slot loads in flight, running straight across tile boundaries (the
+// same ring as the single-token kernel).  In LDS, 16-byte chunk c of token n
+// sits at position c ^ (n % 16) of its 256-column block, so the 16 tokens an
+// instruction reads fall on 16 different bank groups.  Rows too long for LDS
+// take their B operands from global memory (cache-resident: every workgroup
+// reads the same few rows), loaded in the ring next to the weights.  Partial
+// sums of the waves of a tile meet in LDS (double-buffered, one barrier per
+// tile) and the tile's first wave adds them, dequantizes and stores.
 
 #include "group.hpp"
 
 namespace bt {
 
 namespace {
+
+// Launch shape: 8 waves per workgroup, K split over all 8, 4 slot loads in
+// flight per wave.
+constexpr int kMfWaves = 8;
+constexpr int kMfThreads = kMfWaves * kWave;
+constexpr int kMfSplit = 8;
+constexpr int kMfRing = 4;
+// LDS of one compute unit and the part a workgroup may use for token codes.
+constexpr int64_t kLdsPerCu = 160 * 1024;
+constexpr int64_t kMfCodesMax = 136 * 1024;
 
 __device__ __forceinline__ v4i unpack_a(uint32_t word) {
     v4i a;
@@ -31,72 +61,238 @@ __device__ __forceinline__ v4i unpack_a(uint32_t word) {
     return a;
 }
 
-// Each wave owns one 16-row tile and 16*TG tokens; the K loop streams the
-// tile's packed row once and reads activations straight from global memory.
-template <int WAVES, int TG>
+// s_waitcnt immediate: at most n vector-memory operations outstanding and no
+// LDS operation (expcnt left at its maximum).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// One ring entry: a weight slot and, when B comes from global memory, the
+// four B fragments of the same block.
+template <bool GLOBAL_B>
+struct Slot {
+    v4u w;
+    v4i b[GLOBAL_B ? 4 : 1];
+};
+
+// MODE 1: token codes staged in LDS.  MODE 2: read from global memory.
+template <int MODE, int WAVES, int P, int RING>
 __global__ __launch_bounds__(WAVES * kWave)
-void mfma_simple_kernel(GroupArgs a) {
+void decode_mfma_kernel(GroupArgs a) {
+    static_assert(WAVES % P == 0, "K split must divide the waves");
+    constexpr bool kGlobalB = MODE == 2;
+    constexpr int TPW = WAVES / P;  // tiles per workgroup iteration
+    constexpr int kVmPerSlot = kGlobalB ? 5 : 1;  // loads per ring entry
+    static_assert(RING * kVmPerSlot <= 63, "wait count exceeds the counter");
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];  // MODE 1 codes
+    __shared__ v4i red[2][TPW][P > 1 ? P - 1 : 1][kWave];
+    __shared__ __attribute__((aligned(256))) uint32_t s_tab[kWave];
+
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
-    if (tile >= group_tiles(a)) return;  // whole wave
-    const TileRef tr = resolve_tile(a, tile);
     const int64_t K = a.K, qb = K / kTileCols;
     const int r = lane % 16, h = lane / 16;
-    const int64_t nb = (int64_t)blockIdx.y * 16 * TG;
-    gptr<const v4u> wp = to_global(reinterpret_cast<const v4u *>(tr.packed + tr.mt * qb * kTileBytes)) + lane;
+    const int64_t n0 = 16 * (int64_t)blockIdx.y;        // first token of the workgroup
+    const int nrows = (int)min((int64_t)16, a.N - n0);  // its tokens, >= 1
+    // B row of this lane.  Result columns of tokens >= nrows depend only on
+    // their own (clamped) B rows and are never stored.
+    const int rr = min(r, nrows - 1);
+    const int kpart = wave % P, sub = wave / P;
+    const int64_t q0 = qb * kpart / P, q1 = qb * (kpart + 1) / P;
+    const int64_t nq = q1 - q0;  // blocks of this wave per tile (may be 0)
+    const int64_t total = group_tiles(a);
+    const int64_t ngroups = (total + TPW - 1) / TPW;
+    const int64_t nit = (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    auto tile_of = [&](int64_t it) { return (blockIdx.x + it * gridDim.x) * TPW + sub; };
+    const bool has_work = nq > 0 && tile_of(0) < total;
+    const int64_t nslots = has_work ? nit * nq : 0;
 
-    v4i acc[TG];
-#pragma unroll
-    for (int g = 0; g < TG; ++g) acc[g] = v4i{0, 0, 0, 0};
-
-    for (int64_t q = 0; q < qb; ++q) {
-        const v4u p = wp[q * kWave];
-        const uint32_t words[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const v4i A = unpack_a(words[t]);
-#pragma unroll
-            for (int g = 0; g < TG; ++g) {
-                const int64_t n = nb + 16 * g + r;
-                v4i B = v4i{0, 0, 0, 0};
-                if (n < a.N)
-                    B = *reinterpret_cast<const v4i *>(a.xq + n * K + q * kTileCols + 64 * t + 16 * h);
-                acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, acc[g], 0, 0, 0);
-            }
+    // ---- prologue ----
+    // Per-token code sums and activation scales and the weight scales go to
+    // LDS by direct 4-byte loads (no register waits): lane l of every wave
+    // fills s_tab[l] -- [0,16) code sums, [16,32) scales (clamped tokens),
+    // [32,64) weight scale of projection min(l - 32, 2).
+    {
+        const uint8_t *src;
+        if (lane < 32) {
+            const int j = min(lane % 16, nrows - 1);
+            src = lane < 16 ? reinterpret_cast<const uint8_t *>(a.xsum + n0 + j)
+                            : reinterpret_cast<const uint8_t *>(a.xs + n0 + j);
+        } else {
+            const int p = min(lane - 32, kMaxGroup - 1);
+            const uint64_t m1 = p >= 1 ? ~0ull : 0ull, m2 = p >= 2 ? ~0ull : 0ull;
+            const uint8_t *pk = reinterpret_cast<const uint8_t *>(
+                pick3(m1, m2, (uint64_t)a.packed[0], (uint64_t)a.packed[1], (uint64_t)a.packed[2]));
+            const int64_t M = (int64_t)pick3(m1, m2, (uint64_t)a.M[0], (uint64_t)a.M[1],
+                                             (uint64_t)a.M[2]);
+            src = pk + M * K / 4;
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)s_tab, 4, 0, 0);
+    }
+    // Direct loads of the token codes into LDS (MODE 1).  LDS chunk p (16
+    // bytes) = token p / (K/16), position p % (K/16); it holds global chunk
+    // position ^ (token % 16).  Lane l of a 1 KiB unit u fills chunk 64u + l;
+    // units past the rows (allocation rounded up to 1 KiB) re-read the last
+    // chunk.
+    if (MODE == 1) {
+        const int64_t cpr = K / 16;
+        const int64_t chunks = nrows * cpr;
+        const int64_t units = (chunks + 63) / 64;
+        for (int64_t u = wave; u < units; u += WAVES) {
+            const int64_t p = min(64 * u + lane, chunks - 1);
+            const int64_t n = p / cpr, c = p - n * cpr;
+            const int8_t *src = a.xq + (n0 + n) * K + 16 * (c ^ (n & 15));
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(smem + u * 1024), 16, 0, 0);
         }
     }
 
-    const float s_w = packed_scale(tr.packed, tr.M, K);
+    // Load cursor (as in the single-token kernel): slot li = (iteration lit,
+    // block lq); past the last valid slot it stays put, so every ring load is
+    // unconditional and the compiler's wait counts stay exact.
+    int64_t li = 0, lit = 0, lq = q0;
+    bool lvalid = has_work;
+    gptr<const v4u> lp;
+    auto slot_base = [&](int64_t t) {
+        const TileRef tr = resolve_tile(a, t);
+        return to_global(reinterpret_cast<const v4u *>(tr.packed + tr.mt * qb * kTileBytes)) + lane;
+    };
+    // A wave without work points at a valid slot too: every wave issues the
+    // ring fill, so one wait count below holds for all of them.
+    lp = slot_base(has_work ? tile_of(0) : 0) + (has_work ? q0 : 0) * kWave;
+    auto advance_load = [&]() {
+        if (++li >= nslots || !lvalid) return;
+        if (++lq < q1) {
+            lp += kWave;
+            return;
+        }
+        lq = q0;
+        ++lit;
+        const int64_t t = tile_of(lit);
+        if (t < total) lp = slot_base(t) + q0 * kWave;
+        else lvalid = false;
+    };
+    // Global B fragments of block q (MODE 2): row rr of the group.
+    const gptr<const v4i> xrow =
+        to_global(reinterpret_cast<const v4i *>(a.xq + (n0 + rr) * K + 16 * h));
+    auto load_slot = [&](Slot<kGlobalB> &s) {
+        s.w = *lp;
+        if (kGlobalB) {
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
-        const int64_t n = nb + 16 * g + r;
-        if (n < a.N) {
-            const float f = token_factor(s_w, a.xs[n]);
-            const int32_t sub = a.xsum[n];
+            for (int t = 0; t < 4; ++t) s.b[t] = xrow[lq * (kTileCols / 16) + 4 * t];
+        }
+    };
+
+    // RING + 1 entries, RING of them in flight: the loop below consumes entry
+    // d and then refills entry d - 1, so no entry is live twice and the ring
+    // needs no register copies.
+    constexpr int kSlots = RING + 1;
+    Slot<kGlobalB> ring[kSlots];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = tr.mt * kTileRows + 4 * h + v;
-                store_out(tr.y, a.ydt, n * tr.M + m, acc[g][v] - sub, f);
+    for (int d = 0; d < RING; ++d) {
+        load_slot(ring[d]);
+        advance_load();
+    }
+    // Everything but the ring is complete and visible after this.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RING * kVmPerSlot));
+    __builtin_amdgcn_s_barrier();
+
+    // LDS byte offsets of this lane's B fragments at block 0 (MODE 1).
+    int boff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) boff[t] = (int)(rr * K + 16 * ((4 * t + h) ^ rr));
+
+    v4i acc = v4i{0, 0, 0, 0};
+    int buf = 0;
+    // Finish iteration it: the waves of each tile meet in LDS; the tile's
+    // first wave adds the parts, dequantizes and stores.  Every wave calls
+    // this once per iteration, in order (it holds one barrier when P > 1).
+    auto iter_done = [&](int64_t it) {
+        v4i sum = acc;
+        if (P > 1) {
+            if (kpart > 0) red[buf][sub][kpart - 1][lane] = acc;
+            __syncthreads();
+            if (kpart == 0) {
+#pragma unroll
+                for (int p = 0; p < P - 1; ++p) sum += red[buf][sub][p][lane];
+            }
+            buf ^= 1;
+        }
+        acc = v4i{0, 0, 0, 0};
+        const int64_t tile = tile_of(it);
+        if (kpart == 0 && r < nrows && tile < total) {
+            const TileRef tr = resolve_tile(a, tile);
+            const float f = token_factor(__uint_as_float(s_tab[32 + tr.proj]),
+                                         __uint_as_float(s_tab[16 + r]));
+            store_out4(tr.y, a.ydt, (n0 + r) * tr.M + tr.mt * kTileRows + 4 * h, sum,
+                       (int32_t)s_tab[r], f);
+        }
+    };
+
+    if (!has_work) {
+        for (int64_t it = 0; it < nit; ++it) iter_done(it);
+        return;
+    }
+    int64_t cq = q0, cit = 0;  // compute cursor: block, iteration
+    for (int64_t base = 0; base < nslots; base += kSlots) {
+#pragma unroll
+        for (int d = 0; d < kSlots; ++d) {
+            const int64_t i = base + d;
+            if (i < nslots) {
+                const Slot<kGlobalB> &cur = ring[d];
+                const uint32_t words[4] = {cur.w.x, cur.w.y, cur.w.z, cur.w.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v4i B;
+                    if (kGlobalB)
+                        B = cur.b[t];
+                    else
+                        B = *reinterpret_cast<const v4i *>(smem + boff[t] + cq * kTileCols);
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_a(words[t]), B, acc, 0, 0, 0);
+                }
+            }
+            load_slot(ring[(d + RING) % kSlots]);
+            advance_load();
+            if (i < nslots && ++cq == q1) {
+                iter_done(cit);
+                cq = q0;
+                ++cit;
             }
         }
     }
 }
 
-template <int WAVES, int TG>
-hipError_t launch_simple(const GroupArgs &a, hipStream_t s) {
-    const int64_t tiles = group_tiles(a);
-    const dim3 grid((unsigned)((tiles + WAVES - 1) / WAVES),
-                    (unsigned)((a.N + 16 * TG - 1) / (16 * TG)));
-    hipLaunchKernelGGL((mfma_simple_kernel<WAVES, TG>), grid, dim3(WAVES * kWave), 0, s, a);
+template <int MODE>
+hipError_t launch_mf(const GroupArgs &a, size_t shmem, int per_cu, hipStream_t s) {
+    constexpr int TPW = kMfWaves / kMfSplit;
+    auto kern = decode_mfma_kernel<MODE, kMfWaves, kMfSplit, kMfRing>;
+    if (shmem > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)shmem);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t tgroups = (a.N + 15) / 16;
+    const int64_t groups = (group_tiles(a) + TPW - 1) / TPW;
+    const int64_t want = ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups;
+    const int64_t grid = max((int64_t)1, min(groups, want));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid, (unsigned)tgroups), dim3(kMfThreads), shmem, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
-    return launch_simple<4, 4>(a, s);
+    if (a.N <= 0 || group_tiles(a) == 0) return hipSuccess;
+    const int64_t rows = min((int64_t)16, a.N);
+    const int64_t codes = (rows * a.K + 1023) / 1024 * 1024;
+    if (codes <= kMfCodesMax) {
+        // static LDS: partial sums (2 x 7 KiB) and the per-token tables
+        const int64_t lds = codes + 2 * (kMfSplit - 1) * kWave * 16 + 256;
+        const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / lds));
+        return launch_mf<1>(a, (size_t)codes, per_cu, s);
+    }
+    return launch_mf<2>(a, 0, 2, s);
 }
-
 
 }  // namespace bt

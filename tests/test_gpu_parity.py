@@ -129,6 +129,26 @@ def test_matmul_float_within_tolerance(fn, ydt):
             assert_rel_close(as_f64(y), ref["y"], RTOL[ydt], f"{fn} {M}x{K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (48, 10240, 16),    # 16 rows x 10240 columns: too long for LDS, B from global memory
+    (80, 16384, 9),     # 9 rows x 16 KiB: global B, ragged token group
+    (48, 10240, 20),    # two token groups, the second ragged, global B
+    (112, 8192, 8),     # 8 rows x 8 KiB: staged in LDS, two workgroups per CU
+    (48, 8448, 16),     # 16 rows x 8448: staged, one workgroup per CU
+    (32, 768, 33),      # three token groups, one token in the last
+])
+def test_batched_decode_staging_modes(M, K, N):
+    """Both B sources of the batched-decode kernel (codes staged in LDS, or
+    read from global memory when the rows are too long), ragged token groups."""
+    ref_packed, ref, packed, xq, xs, xsum = _case(M, K, N, 7 * M + K + N)
+    for ydt in (bt.BT_I32, bt.BT_F32, bt.BT_BF16):
+        y = bt.gemv(packed, M, K, xq, xs, xsum, ydt)
+        if ydt == bt.BT_I32:
+            assert_equal(to_np(y), ref["acc"], f"M={M} K={K} N={N}")
+        else:
+            assert_rel_close(as_f64(y), ref["y"], RTOL[ydt], f"M={M} K={K} N={N} ydt={ydt}")
+
+
 def test_gemv_and_gemm_agree_bitwise():
     M, K = 208, 2304
     for N in (1, 4, 5, 64, 257):
