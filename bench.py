@@ -6,7 +6,8 @@
 
 A step is one pass of the whole path over one batch: for every layer, each of
 the four projection groups quantizes its input per token (absmax int8) and
-runs its ternary products with the fused dequantization epilogue.  Weights
+runs its ternary products with the fused dequantization epilogue (through the
+per-layer driver: at one token a single launch per layer does all of it).  Weights
 are packed once at load time (not timed; timed separately as "pack").
 Inputs already sit in HBM when the timed region starts.
 
@@ -40,9 +41,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources of each measured kernel: a traffic record is only used while they
 # are unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "decode_dot4_kernel (fused quantization)": ("gemv.hip", "common.hpp", "group.hpp", "quant.hpp"),
-    "decode_dot4_kernel": ("gemv.hip", "common.hpp", "group.hpp", "quant.hpp"),
-    "mfma_decode_kernel": ("mfma.hip", "common.hpp", "group.hpp"),
+    "layer_dot4_kernel": ("layer.hip", "layer.hpp", "dot4.hpp", "common.hpp", "quant.hpp",
+                          "internal.hpp"),
+    "decode_dot4_kernel (fused quantization)": ("gemv.hip", "dot4.hpp", "common.hpp", "group.hpp",
+                                                "quant.hpp"),
+    "decode_dot4_kernel": ("gemv.hip", "dot4.hpp", "common.hpp", "group.hpp", "quant.hpp"),
+    "decode_mfma_kernel": ("mfma.hip", "common.hpp", "group.hpp"),
     "prefill_kernel": ("prefill.hip", "common.hpp", "group.hpp"),
 }
 
@@ -117,6 +121,10 @@ class Model:
         self.ys = [L.alloc_outputs(N, ydt, self.device) for L in self.layer_objs]
         self.ios = [L.make_io(x, y, ydt, self.ws)
                     for L, x, y in zip(self.layer_objs, self.xs, self.ys)]
+        self.ios_pg = [L.make_io(x, y, ydt, self.ws, per_group=True)
+                       for L, x, y in zip(self.layer_objs, self.xs, self.ys)]
+        xdt = bt.BT_BF16 if wl.x_dtype == "bf16" else bt.BT_F32
+        self.one_launch = bt.bt_layer_one_launch(L0.c, N, xdt) == 1
         # quantized copies of every input, for the kernel-only timing pass
         self.q = [[bt.quant_act(x) for x in xs] for xs in self.xs]
         self.groups = []
@@ -134,6 +142,12 @@ class Model:
     def step(self):
         import ternary_weight_quantized_bt_amd as bt
         for L, io in zip(self.layer_objs, self.ios):
+            bt.bt_layer_forward(L.c, io)
+
+    def step_per_group(self):
+        """The same step with every layer run as four group launches."""
+        import ternary_weight_quantized_bt_amd as bt
+        for L, io in zip(self.layer_objs, self.ios_pg):
             bt.bt_layer_forward(L.c, io)
 
     def products_only(self):
@@ -161,22 +175,23 @@ def time_region(fn, reps):
     return start.elapsed_time(end) / 1e3, wall
 
 
-def run_steps(model, steps, warmup, use_graph):
+def run_steps(model, steps, warmup, use_graph, step=None):
     """Returns (seconds per step, wall seconds of the timed region)."""
     import torch
+    step = step or model.step
     if use_graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            model.step()  # eager warm-up on the capture stream
+            step()  # eager warm-up on the capture stream
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            model.step()
+            step()
         fn = g.replay
     else:
-        fn = model.step
+        fn = step
     for _ in range(warmup):
         fn()
     t, wall = time_region(fn, steps)
@@ -304,31 +319,39 @@ def main():
     if use_graph:
         eager_sec, _ = run_steps(model, max(3, args.steps // 4), 2, False)
     # Grouped products alone, on inputs quantized beforehand (same kernels and
-    # grids as the step, minus the fused quantization of the decode path).
+    # grids as the per-group step, minus the quantization).
     kt, launches = kernel_pass(model, max(3, args.steps // 2))
-    launches_per_step = 4 * layers
-    bytes_per_launch = model.packed_bytes / launches_per_step
     ops_step = 2 * N * sum(M * K for M, K in wl.shapes) * layers
     fused = N <= 4 and all(n * k <= 65536 for k in wl.input_widths()
                            for n in [1 if N == 1 else (2 if N == 2 else 4)])
     if decode:
         value = model.packed_bytes / sec / 1e9
         unit = "GB/s"
-        if fused:
-            # The step consists of nothing but these launches (the
-            # quantization is fused into them), so their average duration is
-            # the step time over the launch count, from the HIP events around
-            # the timed region.
+        if model.one_launch:
+            # One launch per layer and nothing else in the step: the kernel's
+            # average duration is the step time over the layer count (HIP
+            # events around the timed region, on the stream the graph runs on).
+            kernel_name = "layer_dot4_kernel"
+            launches_per_step = layers
+            kavg = sec / launches_per_step
+        elif fused:
+            # Four launches per layer with the quantization fused into them:
+            # again nothing else in the step.
             kernel_name = "decode_dot4_kernel (fused quantization)"
+            launches_per_step = 4 * layers
             kavg = sec / launches_per_step
         else:
-            kernel_name = "decode_dot4_kernel" if N <= 4 else "mfma_decode_kernel"
+            kernel_name = "decode_dot4_kernel" if N <= 4 else "decode_mfma_kernel"
+            launches_per_step = 4 * layers
             kavg = kt
+        bytes_per_launch = model.packed_bytes / launches_per_step
         achieved = bytes_per_launch / kavg / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
         kernel_name = "prefill_kernel"
+        launches_per_step = 4 * layers
+        bytes_per_launch = model.packed_bytes / launches_per_step
         kavg = kt
         value = ops_step / sec / 1e12
         unit = "TOPS"
@@ -340,9 +363,16 @@ def main():
     roofline["kernel_avg_us"] = round(kavg * 1e6, 3)
     roofline["launches_per_step"] = launches_per_step
     roofline["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
-    roofline["prequantized_kernel_avg_us"] = round(kt * 1e6, 3)
+    roofline["prequantized_group_kernel_avg_us"] = round(kt * 1e6, 3)
 
     extra = {}
+    if not args.no_extra and decode and model.one_launch:
+        spg, _ = run_steps(model, args.steps, args.warmup, use_graph, model.step_per_group)
+        extra["same_step_per_group_launches"] = {
+            "ms_per_step": round(spg * 1e3, 4),
+            "packed_gb_per_s": round(model.packed_bytes / spg / 1e9, 2),
+            "frac_of_hbm_peak": round(model.packed_bytes / spg / 1e9 / PEAK_HBM_GBS, 4),
+        }
     if not args.no_extra and wl.name == "stream70b" and N == 1:
         model.set_tokens(8)
         s8, _ = run_steps(model, args.steps, args.warmup, use_graph)

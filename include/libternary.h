@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 1
+#define BT_ABI_VERSION 2
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -191,11 +191,21 @@ bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
  *   x[2] (FFN input)        -> gate, up     (K[4] == K[5])
  *   x[3] (FFN hidden)       -> down         (K[6])
  * Each group quantizes its input once (bt_quant_act semantics) and runs its
- * projections; the path (decode or prefill) is chosen from N.  For a few
- * tokens the decode kernel quantizes its input itself (one launch per group);
- * otherwise the codes go through the workspace, whose contents after the call
- * are unspecified.  Outputs are identical to calling bt_quant_act followed by
- * bt_ternary_gemv / bt_ternary_gemm per projection.
+ * projections; the path (decode or prefill) is chosen from N.  Outputs are
+ * identical to calling bt_quant_act followed by bt_ternary_gemv /
+ * bt_ternary_gemm per projection, whatever the launch structure:
+ *   - 1..4 tokens, every K >= 2048, the codes of all four inputs within
+ *     128 KiB and 8-element input chunks within 8 per thread of a 1024-thread
+ *     workgroup (e.g. 1 token of an 8192/28672 block, up to 4 of a
+ *     2560/6912 block): ONE launch for the whole block.  The kernel
+ *     quantizes all four inputs in its prologue and streams the seven
+ *     weight matrices back to back ([PREP] "Stage 1" lists them), so the
+ *     four inputs must all be valid when the call is made -- which is what
+ *     this interface takes.  The workspace is not touched.
+ *   - otherwise, or with BT_LAYER_PER_GROUP in io->flags: one launch per
+ *     group (for a few tokens the decode kernel quantizes its input itself),
+ *     or a quantization launch plus the product, with the codes in the
+ *     workspace, whose contents after the call are unspecified.
  * ---------------------------------------------------------------------- */
 #define BT_LAYER_PROJ 7
 #define BT_LAYER_INPUTS 4
@@ -214,7 +224,11 @@ typedef struct {
     bt_dtype y_dtype;                   /* BT_F32, BT_BF16 or BT_I32 */
     void *workspace;                    /* device scratch, 256-byte aligned */
     size_t workspace_bytes;             /* >= bt_layer_workspace_bytes() */
+    uint32_t flags;                     /* 0 or BT_LAYER_PER_GROUP */
 } bt_layer_io;
+
+/* io->flags: run the four groups as four launches even where one would do. */
+#define BT_LAYER_PER_GROUP 1u
 
 /* Scratch needed by bt_layer_forward for N tokens (quantized inputs, their
  * scales and sums).  Returns 0 if the layer's shapes are invalid. */
@@ -222,6 +236,11 @@ size_t bt_layer_workspace_bytes(const bt_layer *layer, int64_t N);
 
 bt_status bt_layer_forward(const bt_layer *layer, const bt_layer_io *io,
                            bt_stream stream);
+
+/* 1 if bt_layer_forward runs this layer for N tokens of x_dtype as one launch
+ * (without BT_LAYER_PER_GROUP), 0 if as per-group launches, -1 if the layer
+ * or the arguments are invalid.  Host-only; no GPU work. */
+int bt_layer_one_launch(const bt_layer *layer, int64_t N, bt_dtype x_dtype);
 
 #ifdef __cplusplus
 }

@@ -73,7 +73,11 @@ class bt_layer_io(ctypes.Structure):
                 ("y", ctypes.c_void_p * BT_LAYER_PROJ),
                 ("y_dtype", ctypes.c_int),
                 ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
+
+
+BT_LAYER_PER_GROUP = 1
 
 
 _lib = None
@@ -108,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.bt_ternary_matmul_group.argtypes = [ctypes.POINTER(bt_proj), S, I64, P, P,
                                               P, I64, S, P]
         L.bt_ternary_matmul_group.restype = S
+        L.bt_layer_one_launch.argtypes = [ctypes.POINTER(bt_layer), I64, S]
+        L.bt_layer_one_launch.restype = S
         L.bt_layer_workspace_bytes.argtypes = [ctypes.POINTER(bt_layer), I64]
         L.bt_layer_workspace_bytes.restype = ctypes.c_size_t
         L.bt_layer_forward.argtypes = [ctypes.POINTER(bt_layer),
@@ -200,6 +206,10 @@ def make_projs(items):
     return arr
 
 
+def bt_layer_one_launch(layer: bt_layer, N: int, x_dtype: int) -> int:
+    return lib().bt_layer_one_launch(ctypes.byref(layer), N, x_dtype)
+
+
 def bt_layer_workspace_bytes(layer: bt_layer, N: int) -> int:
     return lib().bt_layer_workspace_bytes(ctypes.byref(layer), N)
 
@@ -270,8 +280,9 @@ class Layer:
     def workspace_bytes(self, N: int) -> int:
         return bt_layer_workspace_bytes(self.c, N)
 
-    def make_io(self, xs, ys, y_dtype, workspace) -> bt_layer_io:
+    def make_io(self, xs, ys, y_dtype, workspace, per_group=False) -> bt_layer_io:
         io = bt_layer_io()
+        io.flags = BT_LAYER_PER_GROUP if per_group else 0
         io.N = xs[0].shape[0]
         for i, x in enumerate(xs):
             io.x[i] = _p(x)
@@ -293,13 +304,14 @@ class Layer:
         return torch.empty(max(self.workspace_bytes(N), 256), dtype=torch.uint8,
                            device=device)
 
-    def forward(self, xs, y_dtype=BT_BF16, ys=None, workspace=None, stream=None):
+    def forward(self, xs, y_dtype=BT_BF16, ys=None, workspace=None, stream=None,
+                per_group=False):
         N = xs[0].shape[0]
         dev = xs[0].device
         if ys is None:
             ys = self.alloc_outputs(N, y_dtype, dev)
         if workspace is None:
             workspace = self.alloc_workspace(N, dev)
-        io = self.make_io(xs, ys, y_dtype, workspace)
+        io = self.make_io(xs, ys, y_dtype, workspace, per_group)
         bt_layer_forward(self.c, io, stream)
         return ys

@@ -26,6 +26,9 @@ CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no multiply-add contraction: the activation codes depend on a product
+    # rounded to binary32 before the rounding addition
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -10,6 +10,7 @@
 #include <stdio.h>
 
 #include "internal.hpp"
+#include "layer.hpp"
 
 namespace {
 
@@ -271,6 +272,8 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         return fail(BT_ERR_DTYPE, "%s: x dtype must be BT_F32 or BT_BF16", fn);
     if (io->y_dtype != BT_F32 && io->y_dtype != BT_BF16 && io->y_dtype != BT_I32)
         return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)io->y_dtype);
+    if (io->flags & ~BT_LAYER_PER_GROUP)
+        return fail(BT_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, (unsigned)io->flags);
     if (N == 0) return ok();
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) BT_TRY(check_ptr(io->x[i], "io->x[i]", fn));
     for (int p = 0; p < BT_LAYER_PROJ; ++p) BT_TRY(check_ptr(io->y[p], "io->y[p]", fn));
@@ -281,8 +284,15 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
     if (reinterpret_cast<uintptr_t>(io->workspace) & 255u)
         return fail(BT_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
 
-    const LayerWs ws = carve(Kin, N, io->workspace);
     hipStream_t s = as_stream(stream);
+    if (!(io->flags & BT_LAYER_PER_GROUP) && N < BT_PREFILL_MIN_N &&
+        bt::layer_fusable(Kin, L->M, N, io->x_dtype)) {
+        // one launch for the whole block
+        const bt::LayerArgs la = bt::make_layer_args(L->w, L->M, Kin, io->x, io->y, N, io->y_dtype);
+        const hipError_t e = bt::launch_layer(la, io->x_dtype, s);
+        return e == hipSuccess ? ok() : hip_status(e, fn);
+    }
+    const LayerWs ws = carve(Kin, N, io->workspace);
     // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
     static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
     static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
@@ -311,6 +321,15 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();
+}
+
+int bt_layer_one_launch(const bt_layer *L, int64_t N, bt_dtype x_dtype) {
+    if (L == nullptr || N < 0 || N > BT_MAX_N) return -1;
+    int64_t Kin[BT_LAYER_INPUTS];
+    if (!layer_input_widths(L, Kin)) return -1;
+    for (int p = 0; p < BT_LAYER_PROJ; ++p)
+        if (check_mk(L->M[p], L->K[p], "bt_layer_one_launch") != BT_OK) return -1;
+    return N < BT_PREFILL_MIN_N && bt::layer_fusable(Kin, L->M, N, x_dtype) ? 1 : 0;
 }
 
 }  // extern "C"

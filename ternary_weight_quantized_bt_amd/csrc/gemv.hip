@@ -37,6 +37,7 @@
 // down.  The weighted sums are exact multiples of 16 and 4 and are shifted
 // back before the reduction.
 
+#include "dot4.hpp"
 #include "group.hpp"
 #include "quant.hpp"
 
@@ -58,47 +59,6 @@ constexpr int64_t kDecLdsMax = 64 * 1024;
 // Registers (16-byte units per thread) that hold the raw input of a fused
 // prologue between its two halves.
 constexpr int kRawUnits = 8;
-
-// Per-token accumulators of the three code weights.
-template <int NT>
-struct Acc {
-    int a1[NT];   // weight 1: groups 0 and 3
-    int a4[NT];   // weight 4: group 2
-    int a16[NT];  // weight 16: group 1
-};
-
-template <int NT>
-__device__ __forceinline__ void acc_zero(Acc<NT> &c) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) c.a1[j] = c.a4[j] = c.a16[j] = 0;
-}
-
-// Adds the dot products of one 16-byte slot (64 codes of one row) with the
-// matching activations of tokens j < nvalid (rows of x are K bytes apart).
-template <int NT>
-__device__ __forceinline__ void dot_slot(const v4u p, const int8_t *x, int64_t K,
-                                         int nvalid, Acc<NT> &c) {
-    const uint32_t words[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t w = words[t];
-        const int g0 = (int)((w >> 6) & kCodeMask);  // code
-        const int g1 = (int)(w & (kCodeMask << 4));  // code << 4
-        const int g2 = (int)(w & (kCodeMask << 2));  // code << 2
-        const int g3 = (int)(w & kCodeMask);         // code
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            if (j >= nvalid) break;
-            const uint4 xv = *reinterpret_cast<const uint4 *>(x + j * K + 64 * t);
-            int s1 = c.a1[j];
-            s1 = __builtin_amdgcn_sdot4(g0, (int)xv.x, s1, false);
-            s1 = __builtin_amdgcn_sdot4(g3, (int)xv.w, s1, false);
-            c.a1[j] = s1;
-            c.a16[j] = __builtin_amdgcn_sdot4(g1, (int)xv.y, c.a16[j], false);
-            c.a4[j] = __builtin_amdgcn_sdot4(g2, (int)xv.z, c.a4[j], false);
-        }
-    }
-}
 
 // This lane's 16 bytes of block q of the row tile tr.
 __device__ __forceinline__ gptr<const v4u> slot_ptr(const TileRef &tr, int64_t qb, int64_t q,

@@ -1,0 +1,481 @@
+// layer.hip -- one launch for all seven projections of a block at decode
+// (a few tokens): the four inputs are quantized in the prologue and a single
+// weight stream runs across every projection's row tiles.
+//
+// What is computed is exactly the per-group path: for each projection p with
+// input group g(p) ({q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3),
+//   y_p[n, m] = (sum_k w_p[m,k] * xq_g[n,k]) * s_w(p) * s_a(g, n) / 127
+// with per-token absmax int8 codes ([PARA] section 5, Quant8 and the figure
+// "BitNet b1.58 Ternary Matrix Multiplication"; [I2S] "How I2_S Kernels
+// Process the Format" for the one per-tensor weight scale).  The codes and
+// every output are bit-identical to the per-group launches.
+//
+// Why one launch.  At one token a block's projections are a few to a hundred
+// MB of weights each; four dependent launches per block leave the memory
+// system idle at every boundary (launch, ramp-up, the tail of the last
+// tiles).  Here the workgroups walk the row tiles of all seven projections
+// laid end to end (projection order q, k, v, o, gate, up, down) with a
+// stride of the grid size, and each wave keeps RING slot loads in flight
+// straight across tile and projection boundaries, so HBM streams from the
+// first tile to the last.  The four inputs are all resident when the layer
+// is called; each workgroup quantizes all of them into LDS up front.
+//
+// Prologue.  The inputs, seen as one sequence of 8-element chunks (input
+// group, then token, then column), are dealt to the waves in contiguous
+// spans of 64 x kLayerUnits chunks, lane l taking every 64th chunk from l
+// (each load one contiguous KiB per wave).  A span touches only a few
+// (group, token) rows (rows are >= 256 chunks long); their boundaries are
+// found with wave-uniform arithmetic, each lane keeps one running max per
+// row, DPP wave reductions (quant.hpp) fold them and one lane per row folds
+// the result into LDS with an atomic max.  After a barrier every chunk is
+// rounded from the registers and its codes stored in LDS; code sums are
+// folded the same way.  The rounding is the one of the standalone
+// quantization kernel (quant.hpp), so the codes are identical.
+//
+// Tiles.  Within a tile the waves split K by 256-column blocks, interleaved
+// (wave p of P takes blocks p, p + P, ..., so at any moment the waves of a
+// tile read neighbouring KiB; every wave gets at least one block of every
+// projection: K >= 256 * P).  Weight slots are loaded non-temporally (each
+// byte is read once).  A lane's 16-byte slot is dotted with
+// its activation words from LDS (v_dot4_i32_i8), the four lanes of a row and
+// then the waves of the tile are reduced (LDS, double-buffered, one barrier
+// per tile), and the epilogue dequantizes.
+
+#include <algorithm>
+
+#include "dot4.hpp"
+#include "layer.hpp"
+#include "quant.hpp"
+
+namespace bt {
+
+namespace {
+
+constexpr int kLayerWaves = 16;
+constexpr int kLayerThreads = kLayerWaves * kWave;
+constexpr int kLayerSplit = 8;  // K split over 8 waves: two tiles per iteration
+constexpr int kLayerRing = 4;
+constexpr int kLayerUnits = 8;  // input chunks held per lane
+constexpr int64_t kLayerLdsMax = 128 * 1024;  // token codes of all four inputs
+constexpr int64_t kLayerMinK = (int64_t)kTileCols * kLayerSplit;  // a block per wave
+// (group, token) rows one wave's 64 * kLayerUnits consecutive chunks can
+// touch: rows are at least kLayerMinK / 8 = 256 chunks long.
+constexpr int kWaveRows = kWave * kLayerUnits / (kLayerMinK / 8) + 2;
+
+// Projection -> input group.
+__host__ __device__ constexpr int proj_group(int p) { return p < 3 ? 0 : (p == 3 ? 1 : (p < 6 ? 2 : 3)); }
+
+// arr[i] for a wave-uniform i, as a chain of selects (no dynamic indexing of
+// the by-value argument block, which would move it to private memory).
+template <typename T, int C>
+__device__ __forceinline__ T sel(const T (&arr)[C], int i) {
+    T v = arr[0];
+#pragma unroll
+    for (int k = 1; k < C; ++k) v = (i == k) ? arr[k] : v;
+    return v;
+}
+
+// A tile of the layer: projection, local row tile, input group.
+struct LTile {
+    int p, g;
+    int64_t mt;
+};
+
+__device__ __forceinline__ LTile layer_tile(const LayerArgs &a, int64_t t) {
+    int p = 0;
+#pragma unroll
+    for (int i = 0; i < kLayerProj; ++i) p += t >= a.tend[i] ? 1 : 0;
+    int64_t start = 0;
+#pragma unroll
+    for (int i = 1; i < kLayerProj; ++i) start = (p == i) ? a.tend[i - 1] : start;
+    return LTile{p, proj_group(p), t - start};
+}
+
+// Raw input chunk of 8 elements (global loads only).
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<uint16_t> {
+    v4u a;
+    __device__ __forceinline__ void load(const uint16_t *p) { a = *to_global(reinterpret_cast<const v4u *>(p)); }
+    __device__ __forceinline__ uint32_t abs_bits() const {
+        uint32_t r = 0;
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r = max(r, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+        return r << 16;
+    }
+    __device__ __forceinline__ Eight eight() const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        Eight e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e.v[2 * i] = __uint_as_float(w[i] << 16);
+            e.v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        return e;
+    }
+};
+template <typename T, int NT, int WAVES, int P, int RING>
+__global__ __launch_bounds__(WAVES * kWave)
+void layer_dot4_kernel(LayerArgs a) {
+    static_assert(WAVES % P == 0, "K split must divide the waves");
+    static_assert(16 * NT <= kWave, "one wave stores a tile");
+    static_assert(kLayerProj <= WAVES, "one wave per weight scale");
+    constexpr int TPW = WAVES / P;
+    constexpr int kKeys = kLayerInputs * NT;
+    constexpr int kSpan = kWave * kLayerUnits;  // chunks per wave
+    extern __shared__ __attribute__((aligned(16))) int8_t codes[];
+    __shared__ int red[2][WAVES][NT][16];
+    __shared__ uint32_t s_amax[kKeys];  // max |x| bits per (group, token)
+    __shared__ uint32_t s_sum[kKeys];   // code sum per (group, token)
+    __shared__ float s_ws[kLayerProj];  // weight scales
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int h = lane / 16;
+    const int nvalid = (int)min((int64_t)NT, a.N);
+    const int kpart = wave % P, sub = wave / P;
+    const int64_t total = a.tend[kLayerProj - 1];
+    const int64_t ngroups = (total + TPW - 1) / TPW;
+    const int64_t nit = (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x;
+    auto tile_of = [&](int64_t it) { return (blockIdx.x + it * gridDim.x) * TPW + sub; };
+    // Blocks of this wave in a tile of input group g: q0, q0 + P, ... < q1
+    // (interleaved, so the waves of a tile read consecutive KiB together;
+    // every wave gets at least one block: K >= 256 * P).
+    auto krange = [&](int g, int64_t &q0, int64_t &q1) {
+        const int64_t qb = sel(a.K, g) / kTileCols;
+        q0 = kpart;
+        q1 = kpart + P * ((qb - kpart + P - 1) / P);
+    };
+
+    // Slots of this wave: its tiles of group g are those of the sequence
+    // o + it*S (it >= 0) inside the group's tile range.
+    int64_t nslots = 0;
+    {
+        const int64_t o = (int64_t)blockIdx.x * TPW + sub, S = (int64_t)gridDim.x * TPW;
+        auto upto = [&](int64_t x) { return x <= o ? (int64_t)0 : (x - o + S - 1) / S; };
+        int64_t prev = 0;
+#pragma unroll
+        for (int g = 0; g < kLayerInputs; ++g) {
+            const int64_t end = a.gend[g];
+            int64_t q0, q1;
+            krange(g, q0, q1);
+            nslots += (upto(end) - upto(prev)) * ((q1 - q0) / P);
+            prev = end;
+        }
+    }
+    const bool has_work = tile_of(0) < total;
+
+    // ---- prologue, part 1: this wave's input chunks into registers ----
+    // Wave w owns chunks [w * kSpan, (w + 1) * kSpan) of the sequence; lane l
+    // holds chunks w * kSpan + 64c + l (c < kLayerUnits), so every load is one
+    // contiguous KiB per wave.  The (at most kWaveRows) rows the span touches
+    // are found with wave-uniform arithmetic: row r starts at span offset
+    // st[r] and a chunk at offset d lies in row #{r >= 1 : d >= st[r]}.
+    const int64_t units = a.uoff[kLayerInputs];
+    const int64_t u0 = (int64_t)wave * kSpan;
+    const int nlive = (int)max((int64_t)0, min((int64_t)kSpan, units - u0));
+    const T *rsrc[kWaveRows];  // element of span offset 0 in row r's layout
+    int rdst[kWaveRows];       // LDS byte of span offset 0 in row r's layout
+    int rkey[kWaveRows];       // group * NT + token of row r
+    int st[kWaveRows];         // span offset where row r starts
+    int nrow = 0;              // rows with live chunks
+    {
+        const int64_t u = min(u0, units - 1);
+        int g = 0;
+#pragma unroll
+        for (int i = 1; i < kLayerInputs; ++i) g += u >= a.uoff[i] ? 1 : 0;
+        int64_t cpr = sel(a.K, g) / 8;
+        int64_t j = (u - sel(a.uoff, g)) / cpr;
+        int64_t start = sel(a.uoff, g) + j * cpr - u0;  // <= 0
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r) {
+            const bool real = g < kLayerInputs;
+            const int gg = real ? g : kLayerInputs - 1;
+            const int64_t Kg = sel(a.K, gg);
+            st[r] = real ? (int)start : INT32_MAX;
+            rkey[r] = real ? g * NT + (int)j : 0;
+            // (integer arithmetic: the base may lie before the buffer; only
+            // base + 8d for offsets d inside the row is ever dereferenced)
+            rsrc[r] = reinterpret_cast<const T *>(
+                reinterpret_cast<uintptr_t>(sel(a.x, gg)) +
+                (uintptr_t)((j * Kg - 8 * start) * (int64_t)sizeof(T)));
+            rdst[r] = (int)(sel(a.xoff, gg) + j * Kg - 8 * start);
+            nrow += (real && start < nlive) ? 1 : 0;
+            start += cpr;
+            if (++j == a.N) {
+                j = 0;
+                ++g;
+                cpr = g < kLayerInputs ? sel(a.K, g) / 8 : 1;
+            }
+        }
+    }
+    // Dead chunks (past the sequence) re-read the last chunk of the last row.
+    const T *last = static_cast<const T *>(a.x[kLayerInputs - 1]) +
+                    a.N * a.K[kLayerInputs - 1] - 8;
+    Chunk<T> raw[kLayerUnits];
+    int rowof[kLayerUnits];
+#pragma unroll
+    for (int c = 0; c < kLayerUnits; ++c) {
+        const int d = kWave * c + lane;
+        int r = 0;
+        const T *src = rsrc[0];
+#pragma unroll
+        for (int k = 1; k < kWaveRows; ++k) {
+            r += d >= st[k] ? 1 : 0;
+            src = d >= st[k] ? rsrc[k] : src;
+        }
+        raw[c].load(d < nlive ? src + 8 * d : last);
+        rowof[c] = r;
+    }
+    // Weight scale of projection min(wave, 6) (from its packed tail).
+    const int wp = min(wave, kLayerProj - 1);
+    const float ws = *to_global(reinterpret_cast<const float *>(
+        sel(a.packed, wp) + sel(a.M, wp) * sel(a.K, proj_group(wp)) / 4));
+    if (threadIdx.x < kKeys) {
+        s_amax[threadIdx.x] = 0;
+        s_sum[threadIdx.x] = 0;
+    }
+
+    // Load cursor: tile iteration lit, block lq (< lq1, stepping by P) of that tile;
+    // past the last valid slot it stays put (every ring load unconditional).
+    int64_t li = 0, lit = 0, lq = 0, lq1 = 0;
+    bool lvalid = has_work;
+    gptr<const v4u> lp;
+    auto point = [&](int64_t t) {
+        const LTile lt = layer_tile(a, t);
+        int64_t q0, q1;
+        krange(lt.g, q0, q1);
+        const int64_t qb = sel(a.K, lt.g) / kTileCols;
+        lq = q0;
+        lq1 = q1;
+        lp = to_global(reinterpret_cast<const v4u *>(sel(a.packed, lt.p) +
+                                                     (lt.mt * qb + q0) * kTileBytes)) + lane;
+    };
+    point(has_work ? tile_of(0) : 0);
+    auto advance_load = [&]() {
+        if (++li >= nslots || !lvalid) return;
+        if ((lq += P) < lq1) {
+            lp += kWave * P;
+            return;
+        }
+        const int64_t t = tile_of(++lit);
+        if (t < total) point(t);
+        else lvalid = false;
+    };
+    constexpr int kSlots = RING + 1;
+    v4u ring[kSlots];
+#pragma unroll
+    for (int d = 0; d < RING; ++d) {
+        ring[d] = __builtin_nontemporal_load(lp);
+        advance_load();
+    }
+    __syncthreads();  // zeroed tables
+
+    // ---- prologue, part 2: absmax per (group, token) ----
+    {
+        uint32_t mx[kWaveRows] = {};
+#pragma unroll
+        for (int c = 0; c < kLayerUnits; ++c) {
+            const uint32_t v = kWave * c + lane < nlive ? raw[c].abs_bits() : 0u;
+#pragma unroll
+            for (int r = 0; r < kWaveRows; ++r) mx[r] = rowof[c] == r ? max(mx[r], v) : mx[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r) {
+            if (r < nrow) {
+                const uint32_t m = wave_reduce<true>(mx[r]);
+                if (lane == 0) atomicMax(&s_amax[rkey[r]], m);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- prologue, part 3: codes into LDS, code sums ----
+    {
+        float inv[kWaveRows];
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r) inv[r] = quant_inv(__uint_as_float(s_amax[rkey[r]]));
+        int sm[kWaveRows] = {};
+#pragma unroll
+        for (int c = 0; c < kLayerUnits; ++c) {
+            const int d = kWave * c + lane;
+            const int r = rowof[c];
+            float iv = inv[0];
+            int base = rdst[0];
+#pragma unroll
+            for (int k = 1; k < kWaveRows; ++k) {
+                iv = r == k ? inv[k] : iv;
+                base = r == k ? rdst[k] : base;
+            }
+            int part = 0;
+            const uint2 q = quant8(raw[c].eight(), iv, part);
+            if (d < nlive) {
+                *reinterpret_cast<uint2 *>(codes + base + 8 * d) = q;
+#pragma unroll
+                for (int k = 0; k < kWaveRows; ++k) sm[k] += r == k ? part : 0;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kWaveRows; ++r) {
+            if (r < nrow) {
+                const uint32_t sum = wave_reduce<false>((uint32_t)sm[r]);
+                if (lane == 0) atomicAdd(&s_sum[rkey[r]], sum);
+            }
+        }
+        if (wave < kLayerProj && lane == 0) s_ws[wave] = ws;
+    }
+    __syncthreads();
+
+    // ---- tiles ----
+    // Compute cursor: iteration cit, block cq (< cq1, stepping by P) of its tile,
+    // whose input group's codes start at xb.
+    int64_t cit = 0, cq = 0, cq0 = 0, cq1 = 0, cK = 0;
+    const int8_t *xb = codes;
+    auto enter = [&](int64_t it) {
+        const int64_t t = tile_of(it);
+        if (t >= total) return;
+        const LTile lt = layer_tile(a, t);
+        krange(lt.g, cq0, cq1);
+        cq = cq0;
+        cK = sel(a.K, lt.g);
+        xb = codes + sel(a.xoff, lt.g) + 16 * h;
+    };
+    enter(0);
+
+    int buf = 0;
+    Acc<NT> acc;
+    acc_zero(acc);
+    auto iter_done = [&](int64_t it) {
+        int v[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            v[j] = acc_total(acc, j);
+            v[j] += __shfl_xor(v[j], 16, kWave);
+            v[j] += __shfl_xor(v[j], 32, kWave);
+        }
+        acc_zero(acc);
+        if (lane < 16) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) red[buf][wave][j][lane] = v[j];
+        }
+        __syncthreads();
+        // wave s (< TPW) stores the tile of sub-group s: lane = 16 * token + row
+        // (the tile is wave-uniform, so its projection is resolved in scalars)
+        if (wave < TPW) {
+            const int s = wave;
+            const int j = lane / 16, r = lane % 16;
+            const int64_t tile = (blockIdx.x + it * gridDim.x) * TPW + s;
+            if (j < nvalid && tile < total) {
+                const LTile lt = layer_tile(a, tile);
+                int t = 0;
+#pragma unroll
+                for (int p = 0; p < P; ++p) t += red[buf][s * P + p][j][r];
+                const int64_t M = sel(a.M, lt.p);
+                const float f = token_factor(s_ws[lt.p], __uint_as_float(s_amax[lt.g * NT + j]));
+                store_out(sel(a.y, lt.p), a.ydt, j * M + lt.mt * kTileRows + r,
+                          t - (int32_t)s_sum[lt.g * NT + j], f);
+            }
+        }
+        buf ^= 1;
+    };
+
+    if (!has_work) {
+        for (int64_t it = 0; it < nit; ++it) iter_done(it);
+        return;
+    }
+    for (int64_t base = 0; base < nslots; base += kSlots) {
+#pragma unroll
+        for (int d = 0; d < kSlots; ++d) {
+            const int64_t i = base + d;
+            if (i < nslots) dot_slot<NT>(ring[d], xb + cq * kTileCols, cK, nvalid, acc);
+            ring[(d + RING) % kSlots] = __builtin_nontemporal_load(lp);
+            advance_load();
+            if (i < nslots && (cq += P) == cq1) {
+                iter_done(cit);
+                enter(++cit);
+            }
+        }
+    }
+    // Iterations whose tile for this wave's sub-group is past the end (the
+    // other sub-groups' last tiles) still need this wave at the barrier.
+    for (; cit < nit; ++cit) iter_done(cit);
+}
+
+template <typename T, int NT>
+hipError_t launch_layer_t(const LayerArgs &a, size_t lds, hipStream_t s) {
+    auto kern = layer_dot4_kernel<T, NT, kLayerWaves, kLayerSplit, kLayerRing>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    constexpr int TPW = kLayerWaves / kLayerSplit;
+    const int64_t groups = (a.tend[kLayerProj - 1] + TPW - 1) / TPW;
+    const int64_t grid = min(groups, (int64_t)device_cus());
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kLayerThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
+                   bt_dtype xdt) {
+    if (N < 1 || N > 4) return false;
+    if (xdt != BT_BF16) return false;  // f32 chunks would need twice the registers
+    int64_t sumk = 0;
+    for (int g = 0; g < kLayerInputs; ++g) {
+        if (K[g] < kLayerMinK) return false;
+        sumk += K[g];
+    }
+    (void)M;
+    const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
+    if (nt * sumk > kLayerLdsMax) return false;
+    const int64_t units = N * sumk / 8;
+    return units <= (int64_t)kLayerUnits * kLayerThreads;
+}
+
+LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kLayerProj],
+                          const int64_t K[kLayerInputs], const void *const x[kLayerInputs],
+                          void *const y[kLayerProj], int64_t N, bt_dtype ydt) {
+    LayerArgs a{};
+    int64_t end = 0;
+    for (int p = 0; p < kLayerProj; ++p) {
+        a.packed[p] = w[p];
+        a.y[p] = y[p];
+        a.M[p] = M[p];
+        end += M[p] / kTileRows;
+        a.tend[p] = end;
+    }
+    a.gend[0] = a.tend[2];
+    a.gend[1] = a.tend[3];
+    a.gend[2] = a.tend[5];
+    a.gend[3] = a.tend[6];
+    const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
+    int64_t xo = 0, uo = 0;
+    for (int g = 0; g < kLayerInputs; ++g) {
+        a.K[g] = K[g];
+        a.x[g] = x[g];
+        a.xoff[g] = xo;
+        a.uoff[g] = uo;
+        xo += nt * K[g];
+        uo += N * K[g] / 8;
+    }
+    a.xoff[kLayerInputs] = xo;
+    a.uoff[kLayerInputs] = uo;
+    a.N = N;
+    a.ydt = (int)ydt;
+    return a;
+}
+
+hipError_t launch_layer(const LayerArgs &a, bt_dtype xdt, hipStream_t s) {
+    const size_t lds = (size_t)a.xoff[kLayerInputs];
+    if (xdt != BT_BF16) return hipErrorInvalidValue;  // excluded by layer_fusable
+    if (a.N == 1) return launch_layer_t<uint16_t, 1>(a, lds, s);
+    if (a.N == 2) return launch_layer_t<uint16_t, 2>(a, lds, s);
+    return launch_layer_t<uint16_t, 4>(a, lds, s);
+}
+
+}  // namespace bt

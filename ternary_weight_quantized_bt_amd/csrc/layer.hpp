@@ -1,0 +1,37 @@
+// layer.hpp -- arguments of the one-launch-per-block decode kernel (seven
+// projections, four input groups).
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bt {
+
+constexpr int kLayerProj = BT_LAYER_PROJ;     // q, k, v, o, gate, up, down
+constexpr int kLayerInputs = BT_LAYER_INPUTS;  // x0 -> q,k,v; x1 -> o; x2 -> gate,up; x3 -> down
+
+struct LayerArgs {
+    const uint8_t *packed[kLayerProj];
+    void *y[kLayerProj];
+    int64_t M[kLayerProj];
+    int64_t tend[kLayerProj];     // prefix sums of the projections' row tiles
+    int64_t gend[kLayerInputs];   // end of each input group's tiles
+    int64_t K[kLayerInputs];
+    const void *x[kLayerInputs];  // float / bf16 inputs [N, K[g]]
+    int64_t xoff[kLayerInputs + 1];  // LDS offset of each group's codes (rows K[g] apart)
+    int64_t uoff[kLayerInputs + 1];  // first 8-element chunk of each group (all tokens)
+    int64_t N;
+    int ydt;
+};
+
+// Whether one launch can run the block: 1..4 tokens, every K at least one
+// 256-column block per wave, all token codes in LDS and all input chunks in
+// registers.
+bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
+                   bt_dtype xdt);
+LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kLayerProj],
+                          const int64_t K[kLayerInputs], const void *const x[kLayerInputs],
+                          void *const y[kLayerProj], int64_t N, bt_dtype ydt);
+hipError_t launch_layer(const LayerArgs &a, bt_dtype xdt, hipStream_t s);
+
+}  // namespace bt

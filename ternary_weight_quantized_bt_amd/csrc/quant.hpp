@@ -7,9 +7,10 @@
 // pages print no formula; the one implemented (stated in libternary.h):
 //   amax = max|x| (float32; exact in any order), inv = 127 / amax (float32,
 //   correctly rounded), xq = clamp(rne(x * inv), -127, 127) with a float32
-//   multiply and round-half-to-even, scale = amax, sum = sum of xq.
-// __fdiv_rn / __fmul_rn pin the division and the product whatever the
-// compiler flags; rintf is round-half-to-even.
+//   multiply and round-half-to-even, scale = amax, sum = sum of xq (and the
+//   limit 127 * sign(x) where 127 / amax overflows).
+// __fdiv_rn / __fmul_rn / __fadd_rn pin the division, the product and the
+// rounding addition whatever the compiler flags (no contraction into fma).
 #pragma once
 
 #include "common.hpp"
@@ -100,30 +101,77 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// 127 / amax, or 0 for an all-zero token (every code is then 0).
+// 127 / amax, or 0 for an all-zero token (every code is then 0).  amax is
+// non-negative; its bits are tested so that a subnormal amax is never taken
+// for zero, whatever the denormal mode.
 __device__ __forceinline__ float quant_inv(float amax) {
-    return amax == 0.0f ? 0.0f : __fdiv_rn(127.0f, amax);
+    return __float_as_uint(amax) == 0u ? 0.0f : __fdiv_rn(127.0f, amax);
 }
 
-__device__ __forceinline__ int quant1(float x, float inv) {
-    float r = rintf(__fmul_rn(x, inv));
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+// Round-half-even of x * inv, clamped to [-127, 127], as an int8 code in the
+// low byte of the result.  For a finite inv (|x| <= amax, so |x * inv| <=
+// 127 * (1 + 2^-24)^2 < 127.5 and the clamp never acts) the product is
+// rounded to binary32 first and then 1.5 * 2^23 is added: in that range a
+// binary32 addition rounds to an integer, half to even, and leaves it in the
+// low mantissa bits, so the low byte of the sum's bits is the code.
+__device__ __forceinline__ uint32_t quant1(float x, float inv) {
+    return __float_as_uint(__fadd_rn(__fmul_rn(x, inv), 12582912.0f));
+}
+
+// The code for an infinite inv (amax below 127 / FLT_MAX): the limit
+// 127 * sign(x), and 0 for x == 0.
+__device__ __forceinline__ uint32_t quant1_limit(float x) {
+    return x > 0.0f ? 127u : (x < 0.0f ? 0xFFFFFF81u : 0u);
+}
+
+// Low bytes of four words as one little-endian int8x4 word (v_perm_b32:
+// selector bytes 0-3 take bytes of the second operand, 4-7 of the first, 12
+// gives zero).
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // Quantize eight values into two little-endian int8x4 words; adds the codes
-// to `sum`.
+// to `sum` (a signed dot product of each word with ones).
 __device__ __forceinline__ uint2 quant8(const Eight &e, float inv, int &sum) {
-    uint32_t lo = 0, hi = 0;
+    uint32_t q[8];
+    if (__builtin_expect(__builtin_isinf(inv), 0)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int a = quant1(e.v[i], inv);
-        const int b = quant1(e.v[4 + i], inv);
-        sum += a + b;
-        lo |= ((uint32_t)a & 0xFFu) << (8 * i);
-        hi |= ((uint32_t)b & 0xFFu) << (8 * i);
+        for (int i = 0; i < 8; ++i) q[i] = quant1_limit(e.v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = quant1(e.v[i], inv);
     }
+    const uint32_t lo = pack4(q[0], q[1], q[2], q[3]);
+    const uint32_t hi = pack4(q[4], q[5], q[6], q[7]);
+    sum = __builtin_amdgcn_sdot4((int)lo, 0x01010101, sum, false);
+    sum = __builtin_amdgcn_sdot4((int)hi, 0x01010101, sum, false);
     return make_uint2(lo, hi);
+}
+
+// Wave-wide maximum or sum of v, returned to every lane (as a scalar), with
+// DPP moves: shifts by 1, 2, 4, 8 lanes within each 16-lane row leave the
+// row's result in its lane 15; broadcasts of lane 15 into rows 1 and 3, then
+// of lane 31 into rows 2 and 3, leave the wave's result in lane 63.  Lanes a
+// move cannot reach contribute the identity (0 for an unsigned max or a sum).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v = MAX ? max(v, t) : v + t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v = MAX ? max(v, t) : v + t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v = MAX ? max(v, t) : v + t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v = MAX ? max(v, t) : v + t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v = MAX ? max(v, t) : v + t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    v = MAX ? max(v, t) : v + t;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 }  // namespace bt

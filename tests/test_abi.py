@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bt.bt_abi_version() == 1
+    assert bt.bt_abi_version() == 2
 
 
 def test_packed_bytes():
@@ -155,8 +155,32 @@ def test_layer_validation():
     with pytest.raises(bt.BtError) as e:
         bt.bt_layer_forward(L, io, stream=0)
     assert e.value.status == bt.BT_ERR_INVALID_ARG
+    io.y[6] = A
+    io.flags = 2  # not a defined flag
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_INVALID_ARG
+    io.flags = bt.BT_LAYER_PER_GROUP
     io.N = 0  # nothing to do
     bt.bt_layer_forward(L, io, stream=0)
+
+
+def test_layer_one_launch_choice():
+    """Host-side choice between the one-launch block kernel and per-group
+    launches (no GPU work)."""
+    big = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192),
+           (28672, 8192), (8192, 28672)]
+    small = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560),
+             (6912, 2560), (2560, 6912)]
+    assert bt.bt_layer_one_launch(_layer(big), 1, bt.BT_BF16) == 1
+    assert bt.bt_layer_one_launch(_layer(big), 2, bt.BT_BF16) == 0   # chunks exceed registers
+    assert bt.bt_layer_one_launch(_layer(big), 1, bt.BT_F32) == 0
+    assert bt.bt_layer_one_launch(_layer(small), 4, bt.BT_BF16) == 1
+    assert bt.bt_layer_one_launch(_layer(small), 5, bt.BT_BF16) == 0
+    assert bt.bt_layer_one_launch(_layer(LAYER), 1, bt.BT_BF16) == 0  # K below 2048
+    bad = list(LAYER)
+    bad[1] = (32, 512)
+    assert bt.bt_layer_one_launch(_layer(bad), 1, bt.BT_BF16) == -1
 
 
 def test_binding_refuses_cpu_tensors():

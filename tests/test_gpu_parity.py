@@ -75,9 +75,32 @@ def test_quant_exact(N, K, dtype, dist, frac, scale):
     assert_equal(to_np(xsum), rsum, "sum")
 
 
+def double_rounding_row(K, amax=100.0):
+    """A row with max |x| = amax whose other values x make the binary32
+    product x * fl(127 / amax) land exactly on a half-integer while the exact
+    product does not: rounding the rounded product (the contract) and
+    rounding the exact product (a fused multiply-add) give different codes."""
+    amax = np.float32(amax)
+    inv = np.float32(np.float32(127.0) / amax)
+    row = np.zeros(K, np.float32)
+    row[0] = amax
+    n = 1
+    for k in range(-126, 127):
+        t = k + 0.5
+        x0 = np.float32(t / float(inv))
+        for x in (np.nextafter(x0, np.float32(-1e9)), x0, np.nextafter(x0, np.float32(1e9))):
+            p64 = float(x) * float(inv)
+            if (float(np.float32(p64)) == t and p64 != t and abs(x) < amax and n < K
+                    and np.floor(p64 + 0.5) != np.rint(np.float32(p64))):
+                row[n] = x
+                n += 1
+    assert n > 64
+    return torch.from_numpy(row)
+
+
 def test_quant_special_rows():
     K = 512
-    x = torch.zeros((6, K), dtype=torch.float32)
+    x = torch.zeros((9, K), dtype=torch.float32)
     x[1, 3] = -2.5                       # single negative max
     x[2] = torch.linspace(-127, 127, K)  # ties at exact .5 after scaling by 1
     x[2, 0] = -127.0
@@ -86,6 +109,9 @@ def test_quant_special_rows():
     x[4, 9] = 1.0
     x[5, 100] = 48.72                    # the outlier row of the worked example
     x[5, :6] = torch.tensor([0.04, -0.11, 48.72, 0.02, -0.15, 0.08])
+    x[6, :4] = torch.tensor([1e-37, -5e-38, 0.0, 2e-38])  # 127/amax overflows
+    x[7, 10:13] = torch.tensor([1e-40, -3e-40, 2e-41])     # subnormal amax
+    x[8] = double_rounding_row(K)                          # product rounds before rint
     xq, xs, xsum = bt.quant_act(x.to(DEV))
     rq, rs, rsum = oracle.quant_act(x.numpy())
     assert_equal(to_np(xq), rq, "xq")

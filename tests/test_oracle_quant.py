@@ -85,3 +85,18 @@ def test_subnormals_quantize_to_zero_without_amax_change():
     xq, s, _ = oracle.quant_act(x)
     assert xq[0].tolist() == [127, 0, 0, 0]
     assert s[0] == 1.0
+
+
+def test_overflowing_reciprocal_takes_the_limit():
+    # amax below 127 / FLT_MAX: 127 / amax is +inf in binary32, so every
+    # nonzero x maps to 127 * sign(x) (the limit of x * 127 / amax, clamped)
+    # and x == 0 to 0, whether amax is normal or subnormal.
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(127.0) / np.float32(1e-37))
+    x = np.array([[1e-37, -5e-38, 0.0, 2e-38, -0.0],
+                  [0.0, 1e-40, -3e-40, 2e-41, 0.0]], np.float32)
+    xq, s, sm = oracle.quant_act(x)
+    assert xq[0].tolist() == [127, -127, 0, 127, 0]
+    assert xq[1].tolist() == [0, 127, -127, 127, 0]
+    assert sm.tolist() == [127, 127]
+    assert s[0] == np.float32(1e-37) and s[1] == np.float32(3e-40)
