@@ -75,22 +75,6 @@ __device__ __forceinline__ T sel(const T (&arr)[C], int i) {
     return v;
 }
 
-// A tile of the layer: projection, local row tile, input group.
-struct LTile {
-    int p, g;
-    int64_t mt;
-};
-
-__device__ __forceinline__ LTile layer_tile(const LayerArgs &a, int64_t t) {
-    int p = 0;
-#pragma unroll
-    for (int i = 0; i < kLayerProj; ++i) p += t >= a.tend[i] ? 1 : 0;
-    int64_t start = 0;
-#pragma unroll
-    for (int i = 1; i < kLayerProj; ++i) start = (p == i) ? a.tend[i - 1] : start;
-    return LTile{p, proj_group(p), t - start};
-}
-
 // Raw input chunk of 8 elements (global loads only).
 template <typename T>
 struct Chunk;
@@ -136,32 +120,42 @@ void layer_dot4_kernel(LayerArgs a) {
     const int h = lane / 16;
     const int nvalid = (int)min((int64_t)NT, a.N);
     const int kpart = wave % P, sub = wave / P;
-    const int64_t total = a.tend[kLayerProj - 1];
-    const int64_t ngroups = (total + TPW - 1) / TPW;
-    const int64_t nit = (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x;
-    auto tile_of = [&](int64_t it) { return (blockIdx.x + it * gridDim.x) * TPW + sub; };
-    // Blocks of this wave in a tile of input group g: q0, q0 + P, ... < q1
-    // (interleaved, so the waves of a tile read consecutive KiB together;
-    // every wave gets at least one block: K >= 256 * P).
-    auto krange = [&](int g, int64_t &q0, int64_t &q1) {
-        const int64_t qb = sel(a.K, g) / kTileCols;
-        q0 = kpart;
-        q1 = kpart + P * ((qb - kpart + P - 1) / P);
+    // Tile bookkeeping in 32-bit scalars: tile and slot counts are far below
+    // 2^31, and 64-bit compares would run on the vector unit.
+    const int total = a.tend32[kLayerProj - 1];
+    const int ngroups = (total + TPW - 1) / TPW;
+    const int nit = (ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    auto tile_of = [&](int it) { return ((int)blockIdx.x + it * (int)gridDim.x) * TPW + sub; };
+    // This wave's blocks in a tile of input group g: kpart, kpart + P, ...
+    // (interleaved, so the waves of a tile read neighbouring KiB together),
+    // nq(g) of them, at least one (K >= 256 * P).
+    auto nq = [&](int g) { return (sel(a.qb32, g) - kpart + P - 1) / P; };
+    // Projection of a tile index that only grows (each cursor below walks
+    // its tiles in order): re-resolved only when the tile leaves the current
+    // projection's tile range [start, end).
+    struct Win {
+        int p, start, end;
+    };
+    auto win0 = [&]() { return Win{0, 0, a.tend32[0]}; };
+    auto seek = [&](Win &w, int t) {
+        while (t >= w.end) {
+            ++w.p;
+            w.start = w.end;
+            w.end = sel(a.tend32, w.p);
+        }
     };
 
     // Slots of this wave: its tiles of group g are those of the sequence
     // o + it*S (it >= 0) inside the group's tile range.
-    int64_t nslots = 0;
+    int nslots = 0;
     {
-        const int64_t o = (int64_t)blockIdx.x * TPW + sub, S = (int64_t)gridDim.x * TPW;
-        auto upto = [&](int64_t x) { return x <= o ? (int64_t)0 : (x - o + S - 1) / S; };
-        int64_t prev = 0;
+        const int o = (int)blockIdx.x * TPW + sub, S = (int)gridDim.x * TPW;
+        auto upto = [&](int x) { return x <= o ? 0 : (x - o + S - 1) / S; };
+        int prev = 0;
 #pragma unroll
         for (int g = 0; g < kLayerInputs; ++g) {
-            const int64_t end = a.gend[g];
-            int64_t q0, q1;
-            krange(g, q0, q1);
-            nslots += (upto(end) - upto(prev)) * ((q1 - q0) / P);
+            const int end = a.gend32[g];
+            nslots += (upto(end) - upto(prev)) * nq(g);
             prev = end;
         }
     }
@@ -238,31 +232,35 @@ void layer_dot4_kernel(LayerArgs a) {
         s_sum[threadIdx.x] = 0;
     }
 
-    // Load cursor: tile iteration lit, block lq (< lq1, stepping by P) of that tile;
-    // past the last valid slot it stays put (every ring load unconditional).
-    int64_t li = 0, lit = 0, lq = 0, lq1 = 0;
-    bool lvalid = has_work;
+    // Load cursor: tile iteration lit, lrem slots left in its tile (the
+    // current one included), lleft slots left to load.  On the last slot it
+    // stays put, so every ring load is unconditional (a harmless reload).
+    int lit = 0, lrem = 0, lleft = nslots;
     gptr<const v4u> lp;
-    auto point = [&](int64_t t) {
-        const LTile lt = layer_tile(a, t);
-        int64_t q0, q1;
-        krange(lt.g, q0, q1);
-        const int64_t qb = sel(a.K, lt.g) / kTileCols;
-        lq = q0;
-        lq1 = q1;
-        lp = to_global(reinterpret_cast<const v4u *>(sel(a.packed, lt.p) +
-                                                     (lt.mt * qb + q0) * kTileBytes)) + lane;
+    Win lw = win0();
+    int lnq = 0, lqb = 0;
+    const uint8_t *lbase = nullptr;
+    auto point = [&](int t) {
+        if (t >= lw.end || lbase == nullptr) {
+            seek(lw, t);
+            const int g = proj_group(lw.p);
+            lnq = nq(g);
+            lqb = sel(a.qb32, g);
+            lbase = sel(a.packed, lw.p);
+        }
+        lrem = lnq;
+        lp = to_global(reinterpret_cast<const v4u *>(
+                 lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kTileBytes)) + lane;
     };
     point(has_work ? tile_of(0) : 0);
     auto advance_load = [&]() {
-        if (++li >= nslots || !lvalid) return;
-        if ((lq += P) < lq1) {
+        if (lleft <= 1) return;
+        --lleft;
+        if (--lrem > 0) {
             lp += kWave * P;
             return;
         }
-        const int64_t t = tile_of(++lit);
-        if (t < total) point(t);
-        else lvalid = false;
+        point(tile_of(++lit));
     };
     constexpr int kSlots = RING + 1;
     v4u ring[kSlots];
@@ -329,25 +327,33 @@ void layer_dot4_kernel(LayerArgs a) {
     __syncthreads();
 
     // ---- tiles ----
-    // Compute cursor: iteration cit, block cq (< cq1, stepping by P) of its tile,
-    // whose input group's codes start at xb.
-    int64_t cit = 0, cq = 0, cq0 = 0, cq1 = 0, cK = 0;
+    // Compute cursor: iteration cit, block cq (stepping by P) of its tile,
+    // crem slots left in it, whose input group's codes start at xb.
+    int cit = 0, cq = 0, crem = 0, cK = 0, cnq = 0;
     const int8_t *xb = codes;
-    auto enter = [&](int64_t it) {
-        const int64_t t = tile_of(it);
+    Win cw = win0();
+    bool cfirst = true;
+    auto enter = [&](int it) {
+        const int t = tile_of(it);
         if (t >= total) return;
-        const LTile lt = layer_tile(a, t);
-        krange(lt.g, cq0, cq1);
-        cq = cq0;
-        cK = sel(a.K, lt.g);
-        xb = codes + sel(a.xoff, lt.g) + 16 * h;
+        if (t >= cw.end || cfirst) {
+            seek(cw, t);
+            const int g = proj_group(cw.p);
+            cnq = nq(g);
+            cK = sel(a.k32, g);
+            xb = codes + sel(a.xoff32, g) + 16 * h;
+            cfirst = false;
+        }
+        cq = kpart;
+        crem = cnq;
     };
     enter(0);
 
     int buf = 0;
+    Win ow = win0();  // the tiles this wave stores (waves < TPW)
     Acc<NT> acc;
     acc_zero(acc);
-    auto iter_done = [&](int64_t it) {
+    auto iter_done = [&](int it) {
         int v[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -366,35 +372,41 @@ void layer_dot4_kernel(LayerArgs a) {
         if (wave < TPW) {
             const int s = wave;
             const int j = lane / 16, r = lane % 16;
-            const int64_t tile = (blockIdx.x + it * gridDim.x) * TPW + s;
-            if (j < nvalid && tile < total) {
-                const LTile lt = layer_tile(a, tile);
-                int t = 0;
+            const int tile = ((int)blockIdx.x + it * (int)gridDim.x) * TPW + s;
+            if (tile < total) {
+                seek(ow, tile);
+                if (j < nvalid) {
+                    const int p = ow.p, g = proj_group(p);
+                    int t = 0;
 #pragma unroll
-                for (int p = 0; p < P; ++p) t += red[buf][s * P + p][j][r];
-                const int64_t M = sel(a.M, lt.p);
-                const float f = token_factor(s_ws[lt.p], __uint_as_float(s_amax[lt.g * NT + j]));
-                store_out(sel(a.y, lt.p), a.ydt, j * M + lt.mt * kTileRows + r,
-                          t - (int32_t)s_sum[lt.g * NT + j], f);
+                    for (int q = 0; q < P; ++q) t += red[buf][s * P + q][j][r];
+                    const int64_t M = sel(a.M, p);
+                    const float f = token_factor(s_ws[p], __uint_as_float(s_amax[g * NT + j]));
+                    store_out(sel(a.y, p), a.ydt, j * M + (int64_t)(tile - ow.start) * kTileRows + r,
+                              t - (int32_t)s_sum[g * NT + j], f);
+                }
             }
         }
         buf ^= 1;
     };
 
     if (!has_work) {
-        for (int64_t it = 0; it < nit; ++it) iter_done(it);
+        for (int it = 0; it < nit; ++it) iter_done(it);
         return;
     }
-    for (int64_t base = 0; base < nslots; base += kSlots) {
+    for (int base = 0; base < nslots; base += kSlots) {
 #pragma unroll
         for (int d = 0; d < kSlots; ++d) {
-            const int64_t i = base + d;
+            const int i = base + d;
             if (i < nslots) dot_slot<NT>(ring[d], xb + cq * kTileCols, cK, nvalid, acc);
             ring[(d + RING) % kSlots] = __builtin_nontemporal_load(lp);
             advance_load();
-            if (i < nslots && (cq += P) == cq1) {
-                iter_done(cit);
-                enter(++cit);
+            if (i < nslots) {
+                cq += P;
+                if (--crem == 0) {
+                    iter_done(cit);
+                    enter(++cit);
+                }
             }
         }
     }
@@ -430,7 +442,9 @@ bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], i
         if (K[g] < kLayerMinK) return false;
         sumk += K[g];
     }
-    (void)M;
+    int64_t tiles = 0;
+    for (int p = 0; p < kLayerProj; ++p) tiles += M[p] / kTileRows;
+    if (tiles >= (int64_t)1 << 30) return false;  // tile bookkeeping is 32-bit
     const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
     if (nt * sumk > kLayerLdsMax) return false;
     const int64_t units = N * sumk / 8;
@@ -465,6 +479,13 @@ LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kL
     }
     a.xoff[kLayerInputs] = xo;
     a.uoff[kLayerInputs] = uo;
+    for (int p = 0; p < kLayerProj; ++p) a.tend32[p] = (int)a.tend[p];
+    for (int g = 0; g < kLayerInputs; ++g) {
+        a.gend32[g] = (int)a.gend[g];
+        a.k32[g] = (int)a.K[g];
+        a.xoff32[g] = (int)a.xoff[g];
+        a.qb32[g] = (int)(a.K[g] / kTileCols);
+    }
     a.N = N;
     a.ydt = (int)ydt;
     return a;

@@ -22,6 +22,12 @@ struct LayerArgs {
     int64_t uoff[kLayerInputs + 1];  // first 8-element chunk of each group (all tokens)
     int64_t N;
     int ydt;
+    // 32-bit copies for the kernel's scalar bookkeeping
+    int tend32[kLayerProj];
+    int gend32[kLayerInputs];
+    int k32[kLayerInputs];
+    int xoff32[kLayerInputs];
+    int qb32[kLayerInputs];  // 256-column blocks per row
 };
 
 // Whether one launch can run the block: 1..4 tokens, every K at least one
