@@ -272,7 +272,15 @@ void layer_dot4_kernel(LayerArgs a) {
     __syncthreads();  // zeroed tables
 
     // ---- prologue, part 2: absmax per (group, token) ----
-    {
+    if (nrow == 1) {
+        // the whole span lies in one row (the common case for long rows)
+        uint32_t m = 0;
+#pragma unroll
+        for (int c = 0; c < kLayerUnits; ++c)
+            m = max(m, kWave * c + lane < nlive ? raw[c].abs_bits() : 0u);
+        const uint32_t mw = wave_reduce<true>(m);
+        if (lane == 0) atomicMax(&s_amax[rkey[0]], mw);
+    } else {
         uint32_t mx[kWaveRows] = {};
 #pragma unroll
         for (int c = 0; c < kLayerUnits; ++c) {
@@ -291,7 +299,23 @@ void layer_dot4_kernel(LayerArgs a) {
     __syncthreads();
 
     // ---- prologue, part 3: codes into LDS, code sums ----
-    {
+    const float inv0 = quant_inv(__uint_as_float(s_amax[rkey[0]]));
+    if (nrow == 1 && !__builtin_isinf(inv0)) {
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < kLayerUnits; ++c) {
+            const int d = kWave * c + lane;
+            int part = 0;
+            const uint2 q = quant8_finite(raw[c].eight(), inv0, part);
+            if (d < nlive) {
+                *reinterpret_cast<uint2 *>(codes + rdst[0] + 8 * d) = q;
+                sum += part;
+            }
+        }
+        const uint32_t sw = wave_reduce<false>((uint32_t)sum);
+        if (lane == 0) atomicAdd(&s_sum[rkey[0]], sw);
+    } else {
+        // the span crosses rows (short rows), or 127 / amax overflows
         float inv[kWaveRows];
 #pragma unroll
         for (int r = 0; r < kWaveRows; ++r) inv[r] = quant_inv(__uint_as_float(s_amax[rkey[r]]));
@@ -322,8 +346,8 @@ void layer_dot4_kernel(LayerArgs a) {
                 if (lane == 0) atomicAdd(&s_sum[rkey[r]], sum);
             }
         }
-        if (wave < kLayerProj && lane == 0) s_ws[wave] = ws;
     }
+    if (wave < kLayerProj && lane == 0) s_ws[wave] = ws;
     __syncthreads();
 
     // ---- tiles ----

@@ -133,22 +133,34 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
-// Quantize eight values into two little-endian int8x4 words; adds the codes
-// to `sum` (a signed dot product of each word with ones).
-__device__ __forceinline__ uint2 quant8(const Eight &e, float inv, int &sum) {
-    uint32_t q[8];
-    if (__builtin_expect(__builtin_isinf(inv), 0)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = quant1_limit(e.v[i]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = quant1(e.v[i], inv);
-    }
+// Pack eight codes (low bytes) into two little-endian int8x4 words; adds
+// the codes to `sum` (a signed dot product of each word with ones).
+__device__ __forceinline__ uint2 pack8(const uint32_t (&q)[8], int &sum) {
     const uint32_t lo = pack4(q[0], q[1], q[2], q[3]);
     const uint32_t hi = pack4(q[4], q[5], q[6], q[7]);
     sum = __builtin_amdgcn_sdot4((int)lo, 0x01010101, sum, false);
     sum = __builtin_amdgcn_sdot4((int)hi, 0x01010101, sum, false);
     return make_uint2(lo, hi);
+}
+
+// Quantize eight values with a finite inv.
+__device__ __forceinline__ uint2 quant8_finite(const Eight &e, float inv, int &sum) {
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quant1(e.v[i], inv);
+    return pack8(q, sum);
+}
+
+// Quantize eight values into two little-endian int8x4 words; adds the codes
+// to `sum`.
+__device__ __forceinline__ uint2 quant8(const Eight &e, float inv, int &sum) {
+    if (__builtin_expect(__builtin_isinf(inv), 0)) {
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = quant1_limit(e.v[i]);
+        return pack8(q, sum);
+    }
+    return quant8_finite(e, inv, sum);
 }
 
 // Wave-wide maximum or sum of v, returned to every lane (as a scalar), with

@@ -87,3 +87,25 @@ def test_fused_block_repeated_calls_and_zero_token():
     for a, b in zip(first, again):
         assert torch.equal(a, b)
     assert not to_np(first[4])[1].any() and not to_np(first[5])[1].any()
+
+
+@pytest.mark.parametrize("wl", [SPLIT8, SPLIT16], ids=lambda w: w.name)
+def test_fused_block_tiny_token_takes_the_limit(wl):
+    """A token whose 127 / amax overflows (inputs ~1e-39): codes are
+    127 * sign(x) on both launch structures and match the oracle."""
+    ws, packed, L = build(wl)
+    xs = W.layer_inputs(wl, 0, 2)
+    xs[0] = xs[0].float()
+    xs[0][1] *= 1e-39
+    xs[0] = xs[0].to(torch.bfloat16)
+    xd = [x.to(DEV) for x in xs]
+    fused = L.forward(xd, y_dtype=bt.BT_I32)
+    grouped = L.forward(xd, y_dtype=bt.BT_I32, per_group=True)
+    xq, _, _ = oracle.quant_act(x_for_oracle(xs[0]))
+    assert set(np.unique(xq[1])) <= {-127, 0, 127}
+    for p in range(3):  # q, k, v read input 0
+        M, K = wl.shapes[p]
+        ref_packed, _ = oracle.pack(ws[p][0].numpy(), ws[p][1])
+        assert_equal(to_np(fused[p]), oracle.matmul_i32(ref_packed, M, K, xq, None), f"proj {p}")
+    for a, b in zip(fused, grouped):
+        assert torch.equal(a, b)
