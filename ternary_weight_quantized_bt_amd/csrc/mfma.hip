@@ -31,10 +31,11 @@
 // same ring as the single-token kernel).  In LDS, 16-byte chunk c of token n
 // sits at position c ^ (n % 16) of its 256-column block, so the 16 tokens an
 // instruction reads fall on 16 different bank groups.  Rows too long for LDS
-// take their B operands from global memory (cache-resident: every workgroup
-// reads the same few rows), loaded in the ring next to the weights.  Partial
-// sums of the waves of a tile meet in LDS (double-buffered, one barrier per
-// tile) and the tile's first wave adds them, dequantizes and stores.
+// are done in K phases: the codes of one K range at a time, all of the
+// workgroup's tiles over that range, int32 partial sums kept in LDS between
+// phases (exact: the sum is split, not rounded).  Partial sums of the waves
+// of a tile meet in LDS (double-buffered, one barrier per tile) and the
+// tile's first wave adds them, dequantizes and stores.
 
 #include "group.hpp"
 
@@ -50,7 +51,10 @@ constexpr int kMfSplit = 8;
 constexpr int kMfRing = 4;
 // LDS of one compute unit and the part a workgroup may use for token codes.
 constexpr int64_t kLdsPerCu = 160 * 1024;
-constexpr int64_t kMfCodesMax = 136 * 1024;
+constexpr int64_t kMfCodesMax = 128 * 1024;
+// With more than one K phase, iterations per workgroup whose partial sums
+// stay in LDS (1 KiB each).
+constexpr int64_t kMfPhaseTiles = 8;
 
 __device__ __forceinline__ v4i unpack_a(uint32_t word) {
     v4i a;
@@ -65,24 +69,18 @@ __device__ __forceinline__ v4i unpack_a(uint32_t word) {
 // LDS operation (expcnt left at its maximum).
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
-// One ring entry: a weight slot and, when B comes from global memory, the
-// four B fragments of the same block.
-template <bool GLOBAL_B>
-struct Slot {
-    v4u w;
-    v4i b[GLOBAL_B ? 4 : 1];
-};
-
-// MODE 1: token codes staged in LDS.  MODE 2: read from global memory.
-template <int MODE, int WAVES, int P, int RING>
+// The workgroup's K range is cut into nph phases of qph 256-column blocks
+// (the last may be shorter).  One phase's token codes sit in LDS at a time
+// (rows nb * 256 bytes apart); when there is more than one phase, per-tile
+// int32 partial sums carry over in LDS, after the codes, from one phase to
+// the next, and the last phase dequantizes and stores.
+template <int WAVES, int P, int RING>
 __global__ __launch_bounds__(WAVES * kWave)
-void decode_mfma_kernel(GroupArgs a) {
+void decode_mfma_kernel(GroupArgs a, int nph, int qph) {
     static_assert(WAVES % P == 0, "K split must divide the waves");
-    constexpr bool kGlobalB = MODE == 2;
     constexpr int TPW = WAVES / P;  // tiles per workgroup iteration
-    constexpr int kVmPerSlot = kGlobalB ? 5 : 1;  // loads per ring entry
-    static_assert(RING * kVmPerSlot <= 63, "wait count exceeds the counter");
-    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];  // MODE 1 codes
+    static_assert(RING <= 63, "wait count exceeds the counter");
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];  // codes, then partials
     __shared__ v4i red[2][TPW][P > 1 ? P - 1 : 1][kWave];
     __shared__ __attribute__((aligned(256))) uint32_t s_tab[kWave];
 
@@ -96,16 +94,16 @@ void decode_mfma_kernel(GroupArgs a) {
     // their own (clamped) B rows and are never stored.
     const int rr = min(r, nrows - 1);
     const int kpart = wave % P, sub = wave / P;
-    const int64_t q0 = qb * kpart / P, q1 = qb * (kpart + 1) / P;
-    const int64_t nq = q1 - q0;  // blocks of this wave per tile (may be 0)
     const int64_t total = group_tiles(a);
     const int64_t ngroups = (total + TPW - 1) / TPW;
     const int64_t nit = (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x;
     auto tile_of = [&](int64_t it) { return (blockIdx.x + it * gridDim.x) * TPW + sub; };
-    const bool has_work = nq > 0 && tile_of(0) < total;
-    const int64_t nslots = has_work ? nit * nq : 0;
+    // partial sums: after the codes of the largest phase (16-row allocation)
+    const int64_t rows_alloc = min((int64_t)16, a.N);
+    v4i *const part = reinterpret_cast<v4i *>(
+        smem + ((rows_alloc * qph * kTileCols + 1023) & ~(int64_t)1023));
 
-    // ---- prologue ----
+    // ---- per-token tables ----
     // Per-token code sums and activation scales and the weight scales go to
     // LDS by direct 4-byte loads (no register waits): lane l of every wave
     // fills s_tab[l] -- [0,16) code sums, [16,32) scales (clamped tokens),
@@ -128,144 +126,149 @@ void decode_mfma_kernel(GroupArgs a) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                          (__attribute__((address_space(3))) void *)s_tab, 4, 0, 0);
     }
-    // Direct loads of the token codes into LDS (MODE 1).  LDS chunk p (16
-    // bytes) = token p / (K/16), position p % (K/16); it holds global chunk
-    // position ^ (token % 16).  Lane l of a 1 KiB unit u fills chunk 64u + l;
-    // units past the rows (allocation rounded up to 1 KiB) re-read the last
-    // chunk.
-    if (MODE == 1) {
-        const int64_t cpr = K / 16;
-        const int64_t chunks = nrows * cpr;
-        const int64_t units = (chunks + 63) / 64;
-        for (int64_t u = wave; u < units; u += WAVES) {
-            const int64_t p = min(64 * u + lane, chunks - 1);
-            const int64_t n = p / cpr, c = p - n * cpr;
-            const int8_t *src = a.xq + (n0 + n) * K + 16 * (c ^ (n & 15));
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)src,
-                (__attribute__((address_space(3))) void *)(smem + u * 1024), 16, 0, 0);
-        }
-    }
 
-    // Load cursor (as in the single-token kernel): slot li = (iteration lit,
-    // block lq); past the last valid slot it stays put, so every ring load is
-    // unconditional and the compiler's wait counts stay exact.
-    int64_t li = 0, lit = 0, lq = q0;
-    bool lvalid = has_work;
-    gptr<const v4u> lp;
     auto slot_base = [&](int64_t t) {
         const TileRef tr = resolve_tile(a, t);
         return to_global(reinterpret_cast<const v4u *>(tr.packed + tr.mt * qb * kTileBytes)) + lane;
     };
-    // A wave without work points at a valid slot too: every wave issues the
-    // ring fill, so one wait count below holds for all of them.
-    lp = slot_base(has_work ? tile_of(0) : 0) + (has_work ? q0 : 0) * kWave;
-    auto advance_load = [&]() {
-        if (++li >= nslots || !lvalid) return;
-        if (++lq < q1) {
-            lp += kWave;
-            return;
-        }
-        lq = q0;
-        ++lit;
-        const int64_t t = tile_of(lit);
-        if (t < total) lp = slot_base(t) + q0 * kWave;
-        else lvalid = false;
-    };
-    // Global B fragments of block q (MODE 2): row rr of the group.
-    const gptr<const v4i> xrow =
-        to_global(reinterpret_cast<const v4i *>(a.xq + (n0 + rr) * K + 16 * h));
-    auto load_slot = [&](Slot<kGlobalB> &s) {
-        s.w = *lp;
-        if (kGlobalB) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s.b[t] = xrow[lq * (kTileCols / 16) + 4 * t];
-        }
-    };
 
-    // RING + 1 entries, RING of them in flight: the loop below consumes entry
-    // d and then refills entry d - 1, so no entry is live twice and the ring
-    // needs no register copies.
-    constexpr int kSlots = RING + 1;
-    Slot<kGlobalB> ring[kSlots];
-#pragma unroll
-    for (int d = 0; d < RING; ++d) {
-        load_slot(ring[d]);
-        advance_load();
-    }
-    // Everything but the ring is complete and visible after this.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RING * kVmPerSlot));
-    __builtin_amdgcn_s_barrier();
+    for (int ph = 0; ph < nph; ++ph) {
+        const int64_t kb0 = (int64_t)ph * qph;              // first block of the phase
+        const int64_t nb = min((int64_t)qph, qb - kb0);     // its blocks
+        const int64_t q0 = kb0 + nb * kpart / P, q1 = kb0 + nb * (kpart + 1) / P;
+        const int64_t nq = q1 - q0;  // blocks of this wave per tile (may be 0)
+        const bool has_work = nq > 0 && tile_of(0) < total;
+        const int64_t nslots = has_work ? nit * nq : 0;
+        const bool last = ph == nph - 1;
 
-    // LDS byte offsets of this lane's B fragments at block 0 (MODE 1).
-    int boff[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) boff[t] = (int)(rr * K + 16 * ((4 * t + h) ^ rr));
-
-    v4i acc = v4i{0, 0, 0, 0};
-    int buf = 0;
-    // Finish iteration it: the waves of each tile meet in LDS; the tile's
-    // first wave adds the parts, dequantizes and stores.  Every wave calls
-    // this once per iteration, in order (it holds one barrier when P > 1).
-    auto iter_done = [&](int64_t it) {
-        v4i sum = acc;
-        if (P > 1) {
-            if (kpart > 0) red[buf][sub][kpart - 1][lane] = acc;
-            __syncthreads();
-            if (kpart == 0) {
-#pragma unroll
-                for (int p = 0; p < P - 1; ++p) sum += red[buf][sub][p][lane];
+        if (ph > 0) __syncthreads();  // every wave is done with the previous codes
+        // Direct loads of the phase's token codes into LDS.  LDS chunk p (16
+        // bytes) = token p / (nb*16), position c = p % (nb*16) of its row; it
+        // holds the row's chunk (block kb0 + c/16, within-block chunk
+        // (c % 16) ^ (token % 16)).  Lane l of a 1 KiB unit u fills chunk
+        // 64u + l; units past the rows (allocation rounded up to 1 KiB)
+        // re-read the last chunk.
+        {
+            const int64_t cpr = nb * 16;
+            const int64_t chunks = nrows * cpr;
+            const int64_t units = (chunks + 63) / 64;
+            for (int64_t u = wave; u < units; u += WAVES) {
+                const int64_t p = min(64 * u + lane, chunks - 1);
+                const int64_t n = p / cpr, c = p - n * cpr;
+                const int8_t *src = a.xq + (n0 + n) * K + kb0 * kTileCols + 16 * (c ^ (n & 15));
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)src,
+                    (__attribute__((address_space(3))) void *)(smem + u * 1024), 16, 0, 0);
             }
-            buf ^= 1;
         }
-        acc = v4i{0, 0, 0, 0};
-        const int64_t tile = tile_of(it);
-        if (kpart == 0 && r < nrows && tile < total) {
-            const TileRef tr = resolve_tile(a, tile);
-            const float f = token_factor(__uint_as_float(s_tab[32 + tr.proj]),
-                                         __uint_as_float(s_tab[16 + r]));
-            store_out4(tr.y, a.ydt, (n0 + r) * tr.M + tr.mt * kTileRows + 4 * h, sum,
-                       (int32_t)s_tab[r], f);
-        }
-    };
 
-    if (!has_work) {
-        for (int64_t it = 0; it < nit; ++it) iter_done(it);
-        return;
-    }
-    int64_t cq = q0, cit = 0;  // compute cursor: block, iteration
-    for (int64_t base = 0; base < nslots; base += kSlots) {
+        // Load cursor (as in the single-token kernel): slot li = (iteration
+        // lit, block lq); past the last valid slot it stays put, so every
+        // ring load is unconditional and the compiler's wait counts stay
+        // exact.  A wave without work points at a valid slot too.
+        int64_t li = 0, lit = 0, lq = q0;
+        bool lvalid = has_work;
+        gptr<const v4u> lp = slot_base(has_work ? tile_of(0) : 0) + (has_work ? q0 : 0) * kWave;
+        auto advance_load = [&]() {
+            if (++li >= nslots || !lvalid) return;
+            if (++lq < q1) {
+                lp += kWave;
+                return;
+            }
+            lq = q0;
+            ++lit;
+            const int64_t t = tile_of(lit);
+            if (t < total) lp = slot_base(t) + q0 * kWave;
+            else lvalid = false;
+        };
+
+        // RING + 1 entries, RING of them in flight: the loop below consumes
+        // entry d and then refills entry d - 1, so no entry is live twice and
+        // the ring needs no register copies.
+        constexpr int kSlots = RING + 1;
+        v4u ring[kSlots];
 #pragma unroll
-        for (int d = 0; d < kSlots; ++d) {
-            const int64_t i = base + d;
-            if (i < nslots) {
-                const Slot<kGlobalB> &cur = ring[d];
-                const uint32_t words[4] = {cur.w.x, cur.w.y, cur.w.z, cur.w.w};
+        for (int d = 0; d < RING; ++d) {
+            ring[d] = *lp;
+            advance_load();
+        }
+        // Everything but the ring is complete and visible after this.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RING));
+        __builtin_amdgcn_s_barrier();
+
+        // LDS byte offsets of this lane's B fragments at the phase's block 0.
+        int boff[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    v4i B;
-                    if (kGlobalB)
-                        B = cur.b[t];
-                    else
-                        B = *reinterpret_cast<const v4i *>(smem + boff[t] + cq * kTileCols);
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_a(words[t]), B, acc, 0, 0, 0);
+        for (int t = 0; t < 4; ++t) boff[t] = (int)(rr * nb * kTileCols + 16 * ((4 * t + h) ^ rr));
+
+        v4i acc = v4i{0, 0, 0, 0};
+        int buf = 0;
+        // Finish iteration it: the waves of each tile meet in LDS; the tile's
+        // first wave adds the parts (and the earlier phases' partial sum),
+        // then keeps the result for the next phase or dequantizes and
+        // stores.  Every wave calls this once per iteration, in order (it
+        // holds one barrier when P > 1).
+        auto iter_done = [&](int64_t it) {
+            v4i sum = acc;
+            if (P > 1) {
+                if (kpart > 0) red[buf][sub][kpart - 1][lane] = acc;
+                __syncthreads();
+                if (kpart == 0) {
+#pragma unroll
+                    for (int p = 0; p < P - 1; ++p) sum += red[buf][sub][p][lane];
+                }
+                buf ^= 1;
+            }
+            acc = v4i{0, 0, 0, 0};
+            const int64_t tile = tile_of(it);
+            if (kpart == 0 && tile < total) {
+                v4i &keep = part[(it * TPW + sub) * kWave + lane];
+                if (ph > 0) sum += keep;
+                if (!last) {
+                    keep = sum;
+                } else if (r < nrows) {
+                    const TileRef tr = resolve_tile(a, tile);
+                    const float f = token_factor(__uint_as_float(s_tab[32 + tr.proj]),
+                                                 __uint_as_float(s_tab[16 + r]));
+                    store_out4(tr.y, a.ydt, (n0 + r) * tr.M + tr.mt * kTileRows + 4 * h, sum,
+                               (int32_t)s_tab[r], f);
                 }
             }
-            load_slot(ring[(d + RING) % kSlots]);
-            advance_load();
-            if (i < nslots && ++cq == q1) {
-                iter_done(cit);
-                cq = q0;
-                ++cit;
+        };
+
+        if (!has_work) {
+            for (int64_t it = 0; it < nit; ++it) iter_done(it);
+            continue;
+        }
+        int64_t cq = q0, cit = 0;  // compute cursor: block, iteration
+        for (int64_t base = 0; base < nslots; base += kSlots) {
+#pragma unroll
+            for (int d = 0; d < kSlots; ++d) {
+                const int64_t i = base + d;
+                if (i < nslots) {
+                    const uint32_t words[4] = {ring[d].x, ring[d].y, ring[d].z, ring[d].w};
+                    const int8_t *bq = smem + (cq - kb0) * kTileCols;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const v4i B = *reinterpret_cast<const v4i *>(bq + boff[t]);
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_a(words[t]), B, acc, 0, 0, 0);
+                    }
+                }
+                ring[(d + RING) % kSlots] = *lp;
+                advance_load();
+                if (i < nslots && ++cq == q1) {
+                    iter_done(cit);
+                    cq = q0;
+                    ++cit;
+                }
             }
         }
     }
 }
 
-template <int MODE>
-hipError_t launch_mf(const GroupArgs &a, size_t shmem, int per_cu, hipStream_t s) {
-    constexpr int TPW = kMfWaves / kMfSplit;
-    auto kern = decode_mfma_kernel<MODE, kMfWaves, kMfSplit, kMfRing>;
+hipError_t launch_mf(const GroupArgs &a, int nph, int qph, int64_t grid, size_t shmem,
+                     hipStream_t s) {
+    auto kern = decode_mfma_kernel<kMfWaves, kMfSplit, kMfRing>;
     if (shmem > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -273,10 +276,8 @@ hipError_t launch_mf(const GroupArgs &a, size_t shmem, int per_cu, hipStream_t s
         if (e != hipSuccess) return e;
     }
     const int64_t tgroups = (a.N + 15) / 16;
-    const int64_t groups = (group_tiles(a) + TPW - 1) / TPW;
-    const int64_t want = ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups;
-    const int64_t grid = max((int64_t)1, min(groups, want));
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid, (unsigned)tgroups), dim3(kMfThreads), shmem, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid, (unsigned)tgroups), dim3(kMfThreads), shmem, s,
+                       a, nph, qph);
     return hipGetLastError();
 }
 
@@ -284,15 +285,29 @@ hipError_t launch_mf(const GroupArgs &a, size_t shmem, int per_cu, hipStream_t s
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     if (a.N <= 0 || group_tiles(a) == 0) return hipSuccess;
+    constexpr int TPW = kMfWaves / kMfSplit;
     const int64_t rows = min((int64_t)16, a.N);
-    const int64_t codes = (rows * a.K + 1023) / 1024 * 1024;
-    if (codes <= kMfCodesMax) {
-        // static LDS: partial sums (2 x 7 KiB) and the per-token tables
-        const int64_t lds = codes + 2 * (kMfSplit - 1) * kWave * 16 + 256;
-        const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / lds));
-        return launch_mf<1>(a, (size_t)codes, per_cu, s);
+    const int64_t qb = a.K / kTileCols;
+    // phases: as few as keep one phase's codes within kMfCodesMax
+    const int64_t per_block = rows * kTileCols;
+    const int64_t max_blocks = max((int64_t)1, kMfCodesMax / per_block);
+    const int64_t nph = (qb + max_blocks - 1) / max_blocks;
+    const int64_t qph = (qb + nph - 1) / nph;
+    const int64_t codes = (rows * qph * kTileCols + 1023) / 1024 * 1024;
+    // static LDS: partial sums of the waves (2 x 7 KiB) and the token table
+    const int64_t fixed = 2 * (kMfSplit - 1) * kWave * 16 + 256;
+    const int64_t tgroups = (a.N + 15) / 16;
+    const int64_t groups = (group_tiles(a) + TPW - 1) / TPW;
+    int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (codes + fixed)));
+    int64_t grid = max((int64_t)1, min(groups, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups));
+    int64_t partials = 0;
+    if (nph > 1) {
+        // at most kMfPhaseTiles iterations per workgroup keep their partial sums
+        grid = max(grid, (groups + kMfPhaseTiles - 1) / kMfPhaseTiles);
+        const int64_t nit_max = (groups + grid - 1) / grid;
+        partials = nit_max * TPW * kWave * 16;
     }
-    return launch_mf<2>(a, 0, 2, s);
+    return launch_mf(a, (int)nph, (int)qph, grid, (size_t)(codes + partials), s);
 }
 
 }  // namespace bt

@@ -1,11 +1,15 @@
 // quant.hip -- per-token absmax int8 activation quantization kernel.
 //
 // The arithmetic (and its page citations) is in quant.hpp, shared with the
-// fused prologue of the decode kernel.  The code sum lets the products use
+// fused prologues of the decode kernels.  The code sum lets the products use
 // the codes 0/1/2 directly: sum_k (code - 1) * xq = sum_k code * xq - sum xq.
 //
-// One workgroup per token; 256 threads sweep the row twice with 16-byte
-// loads (the second sweep hits L2).
+// One workgroup per token.  Rows of up to 8 * threads * C elements are done
+// in one pass: every thread loads all of its C chunks of 8 elements at once
+// (no load waits on another), the absmax is reduced in registers, across the
+// wave with DPP moves and across the waves through LDS, and the codes are
+// rounded from the registers.  Longer rows sweep the row twice (the second
+// sweep hits L2).
 
 #include "internal.hpp"
 #include "quant.hpp"
@@ -14,34 +18,86 @@ namespace bt {
 
 namespace {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = 512;
 constexpr int kQuantWaves = kQuantThreads / kWave;
 
-template <typename T>
+// Max over the waves' partial maxima / sums written to LDS (after a barrier).
+template <bool MAX>
+__device__ __forceinline__ uint32_t across_waves(const uint32_t (&part)[kQuantWaves]) {
+    uint32_t v = part[0];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) v = MAX ? max(v, part[w]) : v + part[w];
+    return v;
+}
+
+template <typename T, int C>
 __global__ __launch_bounds__(kQuantThreads)
-void quant_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
-                  float *__restrict__ xs, int32_t *__restrict__ xsum) {
+void quant_onepass_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
+                          float *__restrict__ xs, int32_t *__restrict__ xsum) {
     __shared__ uint32_t red_m[kQuantWaves];
-    __shared__ int red_i[kQuantWaves];
+    __shared__ uint32_t red_s[kQuantWaves];
     const int64_t n = blockIdx.x;
     const T *row = x + n * K;
     int8_t *out = xq + n * K;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 
-    uint32_t mbits = 0;
+    // chunk c of this thread starts at element 8 * (threadIdx.x + c * threads);
+    // chunks past the row re-read the last one and are masked
+    Raw8<T> raw[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        raw[c].load(row + min(8 * ((int64_t)threadIdx.x + (int64_t)c * kQuantThreads), K - 8));
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)  // re-read chunks cannot change a max
+        m = max(m, raw[c].abs_bits());
+    m = wave_reduce<true>(m);
+    if (lane == 0) red_m[wave] = m;
+    __syncthreads();
+    const float amax = __uint_as_float(across_waves<true>(red_m));
+    const float inv = quant_inv(amax);
+    int sum = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int64_t k = 8 * ((int64_t)threadIdx.x + (int64_t)c * kQuantThreads);
+        int part = 0;
+        const uint2 q = quant8(raw[c].eight(), inv, part);
+        if (k < K) {
+            *reinterpret_cast<uint2 *>(out + k) = q;
+            sum += part;
+        }
+    }
+    const uint32_t s = wave_reduce<false>((uint32_t)sum);
+    if (lane == 0) red_s[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        xs[n] = amax;
+        xsum[n] = (int32_t)across_waves<false>(red_s);
+    }
+}
+
+// Rows longer than 8 * threads * (largest C): two sweeps.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads)
+void quant_twopass_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
+                          float *__restrict__ xs, int32_t *__restrict__ xsum) {
+    __shared__ uint32_t red_m[kQuantWaves];
+    __shared__ uint32_t red_s[kQuantWaves];
+    const int64_t n = blockIdx.x;
+    const T *row = x + n * K;
+    int8_t *out = xq + n * K;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+
+    uint32_t m = 0;
     for (int64_t k = 8 * (int64_t)threadIdx.x; k < K; k += 8 * kQuantThreads) {
         Raw8<T> r;
         r.load(row + k);
-        mbits = max(mbits, r.abs_bits());
+        m = max(m, r.abs_bits());
     }
-    mbits = wave_max_u32(mbits);
-    if (lane == 0) red_m[wave] = mbits;
+    m = wave_reduce<true>(m);
+    if (lane == 0) red_m[wave] = m;
     __syncthreads();
-    mbits = red_m[0];
-#pragma unroll
-    for (int w = 1; w < kQuantWaves; ++w) mbits = max(mbits, red_m[w]);
-    const float amax = __uint_as_float(mbits);
-
+    const float amax = __uint_as_float(across_waves<true>(red_m));
     const float inv = quant_inv(amax);
     int sum = 0;
     for (int64_t k = 8 * (int64_t)threadIdx.x; k < K; k += 8 * kQuantThreads) {
@@ -49,16 +105,26 @@ void quant_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
         r.load(row + k);
         *reinterpret_cast<uint2 *>(out + k) = quant8(r.eight(), inv, sum);
     }
-    sum = wave_sum(sum);
-    if (lane == 0) red_i[wave] = sum;
+    const uint32_t s = wave_reduce<false>((uint32_t)sum);
+    if (lane == 0) red_s[wave] = s;
     __syncthreads();
     if (threadIdx.x == 0) {
-        int total = 0;
-#pragma unroll
-        for (int w = 0; w < kQuantWaves; ++w) total += red_i[w];
         xs[n] = amax;
-        xsum[n] = total;
+        xsum[n] = (int32_t)across_waves<false>(red_s);
     }
+}
+
+template <typename T>
+hipError_t launch_quant_t(const T *x, int64_t N, int64_t K, int8_t *xq, float *xs,
+                          int32_t *xsum, hipStream_t s) {
+    const int64_t chunks = (K / 8 + kQuantThreads - 1) / kQuantThreads;  // per thread
+    const dim3 grid((unsigned)N), block(kQuantThreads);
+    if (chunks <= 1) hipLaunchKernelGGL((quant_onepass_kernel<T, 1>), grid, block, 0, s, x, K, xq, xs, xsum);
+    else if (chunks <= 2) hipLaunchKernelGGL((quant_onepass_kernel<T, 2>), grid, block, 0, s, x, K, xq, xs, xsum);
+    else if (chunks <= 4) hipLaunchKernelGGL((quant_onepass_kernel<T, 4>), grid, block, 0, s, x, K, xq, xs, xsum);
+    else if (chunks <= 8) hipLaunchKernelGGL((quant_onepass_kernel<T, 8>), grid, block, 0, s, x, K, xq, xs, xsum);
+    else hipLaunchKernelGGL((quant_twopass_kernel<T>), grid, block, 0, s, x, K, xq, xs, xsum);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -66,15 +132,8 @@ void quant_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
 hipError_t launch_quant(const void *x, bt_dtype xdt, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t s) {
     if (N == 0) return hipSuccess;
-    if (xdt == BT_F32)
-        hipLaunchKernelGGL(quant_kernel<float>, dim3((unsigned)N),
-                           dim3(kQuantThreads), 0, s,
-                           static_cast<const float *>(x), K, xq, xs, xsum);
-    else
-        hipLaunchKernelGGL(quant_kernel<uint16_t>, dim3((unsigned)N),
-                           dim3(kQuantThreads), 0, s,
-                           static_cast<const uint16_t *>(x), K, xq, xs, xsum);
-    return hipGetLastError();
+    if (xdt == BT_F32) return launch_quant_t(static_cast<const float *>(x), N, K, xq, xs, xsum, s);
+    return launch_quant_t(static_cast<const uint16_t *>(x), N, K, xq, xs, xsum, s);
 }
 
 }  // namespace bt

@@ -55,7 +55,8 @@ template <>
 struct Raw8<uint16_t> {
     uint4 a;
     __device__ __forceinline__ void load(const uint16_t *p) {
-        a = *reinterpret_cast<const uint4 *>(p);
+        const v4u v = *to_global(reinterpret_cast<const v4u *>(p));
+        a = make_uint4(v.x, v.y, v.z, v.w);
     }
     __device__ __forceinline__ uint32_t abs_bits() const {
         uint32_t r = 0;
@@ -80,8 +81,12 @@ template <>
 struct Raw8<float> {
     float4 a, b;
     __device__ __forceinline__ void load(const float *p) {
-        a = reinterpret_cast<const float4 *>(p)[0];
-        b = reinterpret_cast<const float4 *>(p)[1];
+        const gptr<const v4u> q = to_global(reinterpret_cast<const v4u *>(p));
+        const v4u u = q[0], v = q[1];
+        a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                        __uint_as_float(u.w));
+        b = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                        __uint_as_float(v.w));
     }
     __device__ __forceinline__ uint32_t abs_bits() const {
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};

@@ -175,6 +175,23 @@ def test_batched_decode_staging_modes(M, K, N):
             assert_rel_close(as_f64(y), ref["y"], RTOL[ydt], f"M={M} K={K} N={N} ydt={ydt}")
 
 
+def test_batched_decode_three_k_phases_sampled():
+    """Rows too long for LDS (12 tokens x 25600 columns): three K phases with
+    int32 partial sums carried in LDS, several tiles per workgroup, a ragged
+    last phase; sampled output rows against the oracle."""
+    M, K, N = 9600, 25600, 12
+    w = _w(M, K, 5150)
+    x = _x(N, K, 5151, "bf16", "normal", 0.005, 30.0)
+    ref_packed, _ = oracle.pack(w.numpy(), 0.02)
+    xq_ref, xs_ref, _ = oracle.quant_act(x_for_oracle(x))
+    packed = bt.pack(w.to(DEV), 0.02)
+    xq, xs, xsum = bt.quant_act(x.to(DEV))
+    rows = np.sort(np.random.default_rng(7).choice(M, 96, replace=False))
+    acc = oracle.matmul_i32(ref_packed, M, K, xq_ref, rows)
+    y = to_np(bt.gemv(packed, M, K, xq, xs, xsum, bt.BT_I32))
+    assert_equal(y[:, rows], acc, "three phases")
+
+
 def test_gemv_and_gemm_agree_bitwise():
     M, K = 208, 2304
     for N in (1, 4, 5, 64, 257):
