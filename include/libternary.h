@@ -202,10 +202,15 @@ bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
  *     weight matrices back to back ([PREP] "Stage 1" lists them), so the
  *     four inputs must all be valid when the call is made -- which is what
  *     this interface takes.  The workspace is not touched.
- *   - otherwise, or with BT_LAYER_PER_GROUP in io->flags: one launch per
- *     group (for a few tokens the decode kernel quantizes its input itself),
- *     or a quantization launch plus the product, with the codes in the
- *     workspace, whose contents after the call are unspecified.
+ *   - otherwise: one launch that quantizes the four inputs into the
+ *     workspace (for a few tokens with short rows the per-group decode
+ *     kernel quantizes its own input instead), then one product launch per
+ *     group.
+ *   - with BT_LAYER_PER_GROUP in io->flags: the groups one after the other,
+ *     each quantizing its own input (in the decode kernel, or by a launch of
+ *     its own) before its product -- the order of a decoder whose inputs
+ *     are produced between groups.
+ *   The workspace's contents after the call are unspecified.
  * ---------------------------------------------------------------------- */
 #define BT_LAYER_PROJ 7
 #define BT_LAYER_INPUTS 4

@@ -293,6 +293,27 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         return e == hipSuccess ? ok() : hip_status(e, fn);
     }
     const LayerWs ws = carve(Kin, N, io->workspace);
+    const bool per_group = (io->flags & BT_LAYER_PER_GROUP) != 0;
+    // The four inputs are all valid at the call: unless asked for per-group
+    // launches, the ones that need codes in the workspace are quantized in
+    // one launch up front.
+    bool quantized = false;
+    if (!per_group) {
+        bt::QuantJobs jobs{};
+        int count = 0;
+        for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+            if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, Kin[i], io->x_dtype)) continue;
+            jobs.x[count] = io->x[i];
+            jobs.K[count] = Kin[i];
+            jobs.xq[count] = ws.xq[i];
+            jobs.xs[count] = ws.xs[i];
+            jobs.xsum[count] = ws.xsum[i];
+            ++count;
+        }
+        const hipError_t e = bt::launch_quant_jobs(jobs, count, io->x_dtype, N, s);
+        if (e != hipSuccess) return hip_status(e, fn);
+        quantized = true;
+    }
     // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
     static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
     static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
@@ -314,8 +335,9 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
             // one launch: the decode kernel quantizes its input itself
             e = bt::launch_decode_fused(g, io->x[i], io->x_dtype, s);
         } else {
-            e = bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i], ws.xs[i],
-                                 ws.xsum[i], s);
+            e = quantized ? hipSuccess
+                          : bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i],
+                                             ws.xs[i], ws.xsum[i], s);
             if (e == hipSuccess) e = run_group(g, s);
         }
         if (e != hipSuccess) return hip_status(e, fn);

@@ -15,6 +15,17 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t M, int64_t K,
                          int8_t *w, hipStream_t s);
 hipError_t launch_quant(const void *x, bt_dtype xdt, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t s);
+// Several inputs of N tokens each (widths K[i]) quantized in one launch.
+constexpr int kMaxQuantJobs = 4;
+struct QuantJobs {
+    const void *x[kMaxQuantJobs];
+    int64_t K[kMaxQuantJobs];
+    int8_t *xq[kMaxQuantJobs];
+    float *xs[kMaxQuantJobs];
+    int32_t *xsum[kMaxQuantJobs];
+};
+hipError_t launch_quant_jobs(const QuantJobs &jobs, int count, bt_dtype xdt, int64_t N,
+                             hipStream_t s);
 
 // One projection of a grouped launch.
 struct Proj {

@@ -4,7 +4,8 @@
 // fused prologues of the decode kernels.  The code sum lets the products use
 // the codes 0/1/2 directly: sum_k (code - 1) * xq = sum_k code * xq - sum xq.
 //
-// One workgroup per token.  Rows of up to 8 * threads * C elements are done
+// One workgroup per token and input (several inputs of the same tokens can
+// share one launch).  Rows of up to 8 * threads * C elements are done
 // in one pass: every thread loads all of its C chunks of 8 elements at once
 // (no load waits on another), the absmax is reduced in registers, across the
 // wave with DPP moves and across the waves through LDS, and the codes are
@@ -30,13 +31,29 @@ __device__ __forceinline__ uint32_t across_waves(const uint32_t (&part)[kQuantWa
     return v;
 }
 
+// One-pass quantization of token blockIdx.x of input blockIdx.y.
 template <typename T, int C>
 __global__ __launch_bounds__(kQuantThreads)
-void quant_onepass_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
-                          float *__restrict__ xs, int32_t *__restrict__ xsum) {
+void quant_onepass_kernel(QuantJobs jobs) {
     __shared__ uint32_t red_m[kQuantWaves];
     __shared__ uint32_t red_s[kQuantWaves];
     const int64_t n = blockIdx.x;
+    const int job = __builtin_amdgcn_readfirstlane(blockIdx.y);
+    const T *x = static_cast<const T *>(jobs.x[0]);
+    int8_t *xq = jobs.xq[0];
+    float *xs = jobs.xs[0];
+    int32_t *xsum = jobs.xsum[0];
+    int64_t K = jobs.K[0];
+#pragma unroll
+    for (int i = 1; i < kMaxQuantJobs; ++i) {
+        if (job == i) {
+            x = static_cast<const T *>(jobs.x[i]);
+            xq = jobs.xq[i];
+            xs = jobs.xs[i];
+            xsum = jobs.xsum[i];
+            K = jobs.K[i];
+        }
+    }
     const T *row = x + n * K;
     int8_t *out = xq + n * K;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -114,26 +131,53 @@ void quant_twopass_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict
     }
 }
 
+// All jobs in one launch when every row fits the one-pass kernel (the chunk
+// count is that of the longest row; shorter rows mask the extra chunks),
+// else one two-pass launch per job.
 template <typename T>
-hipError_t launch_quant_t(const T *x, int64_t N, int64_t K, int8_t *xq, float *xs,
-                          int32_t *xsum, hipStream_t s) {
-    const int64_t chunks = (K / 8 + kQuantThreads - 1) / kQuantThreads;  // per thread
-    const dim3 grid((unsigned)N), block(kQuantThreads);
-    if (chunks <= 1) hipLaunchKernelGGL((quant_onepass_kernel<T, 1>), grid, block, 0, s, x, K, xq, xs, xsum);
-    else if (chunks <= 2) hipLaunchKernelGGL((quant_onepass_kernel<T, 2>), grid, block, 0, s, x, K, xq, xs, xsum);
-    else if (chunks <= 4) hipLaunchKernelGGL((quant_onepass_kernel<T, 4>), grid, block, 0, s, x, K, xq, xs, xsum);
-    else if (chunks <= 8) hipLaunchKernelGGL((quant_onepass_kernel<T, 8>), grid, block, 0, s, x, K, xq, xs, xsum);
-    else hipLaunchKernelGGL((quant_twopass_kernel<T>), grid, block, 0, s, x, K, xq, xs, xsum);
+hipError_t launch_quant_t(const QuantJobs &jobs, int count, int64_t N, hipStream_t s) {
+    int64_t kmax = 0;
+    for (int i = 0; i < count; ++i) kmax = max(kmax, jobs.K[i]);
+    const int64_t chunks = (kmax / 8 + kQuantThreads - 1) / kQuantThreads;  // per thread
+    const dim3 grid((unsigned)N, (unsigned)count), block(kQuantThreads);
+    if (chunks <= 1) hipLaunchKernelGGL((quant_onepass_kernel<T, 1>), grid, block, 0, s, jobs);
+    else if (chunks <= 2) hipLaunchKernelGGL((quant_onepass_kernel<T, 2>), grid, block, 0, s, jobs);
+    else if (chunks <= 4) hipLaunchKernelGGL((quant_onepass_kernel<T, 4>), grid, block, 0, s, jobs);
+    else if (chunks <= 8) hipLaunchKernelGGL((quant_onepass_kernel<T, 8>), grid, block, 0, s, jobs);
+    else
+        for (int i = 0; i < count; ++i)
+            hipLaunchKernelGGL(quant_twopass_kernel<T>, dim3((unsigned)N), block, 0, s,
+                               static_cast<const T *>(jobs.x[i]), jobs.K[i], jobs.xq[i], jobs.xs[i],
+                               jobs.xsum[i]);
     return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_quant_jobs(const QuantJobs &jobs, int count, bt_dtype xdt, int64_t N,
+                             hipStream_t s) {
+    if (N == 0 || count == 0) return hipSuccess;
+    QuantJobs j = jobs;
+    for (int i = count; i < kMaxQuantJobs; ++i) {  // unused entries repeat the first
+        j.x[i] = j.x[0];
+        j.K[i] = j.K[0];
+        j.xq[i] = j.xq[0];
+        j.xs[i] = j.xs[0];
+        j.xsum[i] = j.xsum[0];
+    }
+    if (xdt == BT_F32) return launch_quant_t<float>(j, count, N, s);
+    return launch_quant_t<uint16_t>(j, count, N, s);
+}
+
 hipError_t launch_quant(const void *x, bt_dtype xdt, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t s) {
-    if (N == 0) return hipSuccess;
-    if (xdt == BT_F32) return launch_quant_t(static_cast<const float *>(x), N, K, xq, xs, xsum, s);
-    return launch_quant_t(static_cast<const uint16_t *>(x), N, K, xq, xs, xsum, s);
+    QuantJobs j{};
+    j.x[0] = x;
+    j.K[0] = K;
+    j.xq[0] = xq;
+    j.xs[0] = xs;
+    j.xsum[0] = xsum;
+    return launch_quant_jobs(j, 1, xdt, N, s);
 }
 
 }  // namespace bt

@@ -122,3 +122,19 @@ def test_determinism():
         assert torch.equal(a, b)
     for a, b in zip(outs[0], outs[2]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("N", [8, 64, 200])
+def test_quantize_all_inputs_at_once_equals_per_group(N):
+    """The driver quantizes the four inputs in one launch unless asked for
+    per-group launches; both orders give identical outputs."""
+    wl = SMALL
+    ws = W.layer_weights(wl, 0)
+    packed = [bt.pack(w.to(DEV), s) for (w, s) in ws]
+    L = bt.Layer(packed, wl.shapes)
+    xs = [x.to(DEV) for x in W.layer_inputs(wl, 0, N)]
+    for ydt in (bt.BT_I32, bt.BT_BF16):
+        a = L.forward(xs, y_dtype=ydt)
+        b = L.forward(xs, y_dtype=ydt, per_group=True)
+        for p in range(7):
+            assert torch.equal(a[p], b[p]), (N, ydt, p)
