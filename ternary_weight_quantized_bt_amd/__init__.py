@@ -79,6 +79,8 @@ class bt_layer_io(ctypes.Structure):
 
 BT_LAYER_PER_GROUP = 1
 
+# The C ABI version these structures and signatures follow (BT_ABI_VERSION).
+ABI_VERSION = 2
 
 _lib = None
 
@@ -96,6 +98,10 @@ def lib() -> ctypes.CDLL:
         P, I64, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.bt_abi_version.argtypes = []
         L.bt_abi_version.restype = ctypes.c_int
+        if L.bt_abi_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{LIB_PATH} has C ABI version {L.bt_abi_version()}, this binding "
+                f"expects {ABI_VERSION}: rebuild it")
         L.bt_last_error.argtypes = []
         L.bt_last_error.restype = ctypes.c_char_p
         L.bt_packed_bytes.argtypes = [I64, I64]

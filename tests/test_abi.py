@@ -35,7 +35,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert bt.bt_abi_version() == 2
+    header = open(os.path.join(ROOT, "include", "libternary.h")).read()
+    declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 2
 
 
 def test_packed_bytes():
