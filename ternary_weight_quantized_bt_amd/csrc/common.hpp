@@ -51,6 +51,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two float32 -> two bfloat16 (round to nearest even) in one word, low half
+// first: gfx950's packed conversion (v_cvt_pk_bf16_f32), the same bits as
+// f32_to_bf16 for finite inputs.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &b, 4);
+    return u;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
@@ -95,8 +107,7 @@ __device__ __forceinline__ void store_out4(void *y, int ydt, int64_t idx, const 
     } else {
         typedef unsigned v2u __attribute__((ext_vector_type(2)));
         *to_global(reinterpret_cast<v2u *>(reinterpret_cast<uint16_t *>(y) + idx)) =
-            v2u{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
-                (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+            v2u{f32x2_to_bf16x2(v0, v1), f32x2_to_bf16x2(v2, v3)};
     }
 }
 
