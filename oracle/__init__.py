@@ -4,9 +4,12 @@ TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are the only callers.  The GPU library never
 imports this package and this package never imports the GPU library.
 
-The arithmetic lives in ``bt_oracle.c`` (plain C, one element at a time); this
-module only builds it with gcc and passes numpy arrays through ctypes.  The
-readings of the pages it follows are listed in the header of that file.
+The arithmetic of the product path lives in ``bt_oracle.c`` (plain C, one
+element at a time); this module only builds it with gcc and passes numpy
+arrays through ctypes.  The readings of the pages it follows are listed in the
+header of that file.  The float -> ternary weight quantizer (AbsMean and
+max|w| scales, RoundClip) is ``weight_quant.py``: numpy plus exact Python
+integer arithmetic, its readings in its own header.
 
 Sources, cited by page title and section:
   [I2S]  "How BitNet's 1-Bit (I2_S) Quantization Works Compared to Standard
