@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 2
+#define BT_ABI_VERSION 3
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -116,6 +116,39 @@ bt_status bt_pack_ternary(const int8_t *w, int64_t M, int64_t K, float scale,
  * packed tail; read it back with a 4-byte copy from offset M*K/4.) */
 bt_status bt_unpack_ternary(const uint8_t *packed, int64_t M, int64_t K,
                             int8_t *w, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Float -> ternary weight quantizer, straight into the packed layout
+ * ([PARA] section 5, "The Mathematics of BitNet b1.58": the AbsMean
+ * quantizer, gamma = mean |W| and RoundClip; [I2S] "Per-Tensor Scaling
+ * Strategy": the per-tensor scale max|w|).
+ *   s   = mean|W| (BT_WSCALE_ABSMEAN): the exact sum of |W| over all M*K
+ *         entries (bf16 widened exactly) divided by M*K and rounded ONCE to
+ *         the nearest float32, ties to even -- no summation order can
+ *         change it; or max|W| (BT_WSCALE_ABSMAX).
+ *   d   = float32(s + eps)   (eps finite and >= 0; the pages leave it open)
+ *   W~  = RoundClip(float32(W / d), -1, 1) = max(-1, min(1, round(.)))
+ *         with round half to even; 0 / 0 gives 0, nonzero / 0 gives +-1.
+ *   packed = the T16Q256 bytes of W~ with d as the tail scale (what
+ *         bt_pack_ternary(W~, d) writes), so d * W~ approximates W.
+ * w is [M, K] of w_dtype (BT_F32 or BT_BF16) with M * K <= 2^31.  stats, if
+ * not NULL, is a device float[2] that receives {s, d}.  workspace is device
+ * memory of at least bt_quantize_weights_workspace_bytes() bytes, 16-byte
+ * aligned, owned by the caller and used by the call's kernels until they
+ * finish (calls that share a workspace must not overlap).  Non-finite
+ * weights are outside the contract.  Five launches on `stream`, nothing
+ * allocated or synchronized.
+ * ---------------------------------------------------------------------- */
+#define BT_WSCALE_ABSMEAN 0
+#define BT_WSCALE_ABSMAX 1
+#define BT_WQ_WORKSPACE_BYTES 4096
+
+size_t bt_quantize_weights_workspace_bytes(void);
+
+bt_status bt_quantize_weights(const void *w, bt_dtype w_dtype, int64_t M, int64_t K,
+                              int scale_mode, float eps, uint8_t *packed,
+                              float *stats, void *workspace,
+                              size_t workspace_bytes, bt_stream stream);
 
 /* ------------------------------------------------------------------------
  * Per-token absmax int8 activation quantization ([PARA] section 5, Quant8).

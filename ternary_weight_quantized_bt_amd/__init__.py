@@ -78,9 +78,12 @@ class bt_layer_io(ctypes.Structure):
 
 
 BT_LAYER_PER_GROUP = 1
+BT_WSCALE_ABSMEAN = 0
+BT_WSCALE_ABSMAX = 1
+BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -110,6 +113,11 @@ def lib() -> ctypes.CDLL:
         L.bt_pack_ternary.restype = S
         L.bt_unpack_ternary.argtypes = [P, I64, I64, P, P]
         L.bt_unpack_ternary.restype = S
+        L.bt_quantize_weights_workspace_bytes.argtypes = []
+        L.bt_quantize_weights_workspace_bytes.restype = ctypes.c_size_t
+        L.bt_quantize_weights.argtypes = [P, S, I64, I64, S, ctypes.c_float, P, P, P,
+                                          ctypes.c_size_t, P]
+        L.bt_quantize_weights.restype = S
         L.bt_quant_act.argtypes = [P, S, I64, I64, P, P, P, P]
         L.bt_quant_act.restype = S
         for fn in (L.bt_ternary_gemv, L.bt_ternary_gemm):
@@ -180,6 +188,17 @@ def bt_unpack_ternary(packed, M, K, w, stream=None):
     _check(lib().bt_unpack_ternary(_p(packed), M, K, _p(w), _stream(stream)))
 
 
+def bt_quantize_weights_workspace_bytes() -> int:
+    return lib().bt_quantize_weights_workspace_bytes()
+
+
+def bt_quantize_weights(w, w_dtype, M, K, scale_mode, eps, packed, stats, workspace,
+                        workspace_bytes, stream=None):
+    _check(lib().bt_quantize_weights(_p(w), w_dtype, M, K, scale_mode, float(eps),
+                                     _p(packed), _p(stats), _p(workspace),
+                                     workspace_bytes, _stream(stream)))
+
+
 def bt_quant_act(x, x_dtype, N, K, xq, x_scale, x_sum, stream=None):
     _check(lib().bt_quant_act(_p(x), x_dtype, N, K, _p(xq), _p(x_scale),
                               _p(x_sum), _stream(stream)))
@@ -242,6 +261,28 @@ def unpack(packed: torch.Tensor, M: int, K: int, stream=None):
     w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
     bt_unpack_ternary(packed, M, K, w, stream)
     return w
+
+
+def quantize_weights(w: torch.Tensor, mode: str = "absmean", eps: float = 0.0,
+                     stream=None):
+    """float32 / bfloat16 [M, K] device weights -> (packed uint8 tensor with
+    the scale d in its tail, stats float32 [2] = (s, d)); mode "absmean"
+    (s = mean |W|) or "absmax" (s = max |W|), d = s + eps."""
+    M, K = w.shape
+    n = bt_packed_bytes(M, K)
+    if n == 0:
+        raise BtError(BT_ERR_SHAPE, bt_last_error())
+    modes = {"absmean": BT_WSCALE_ABSMEAN, "absmax": BT_WSCALE_ABSMAX}
+    if mode not in modes:
+        raise ValueError(f"mode must be one of {sorted(modes)}")
+    dev = w.device
+    packed = torch.empty(n, dtype=torch.uint8, device=dev)
+    stats = torch.empty(2, dtype=torch.float32, device=dev)
+    ws_bytes = bt_quantize_weights_workspace_bytes()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    bt_quantize_weights(w, _BT_DTYPE[w.dtype], M, K, modes[mode], eps, packed, stats,
+                        ws, ws_bytes, stream)
+    return packed, stats
 
 
 def quant_act(x: torch.Tensor, stream=None):

@@ -167,6 +167,34 @@ bt_status bt_unpack_ternary(const uint8_t *packed, int64_t M, int64_t K, int8_t 
     return hip_status(bt::launch_unpack(packed, M, K, w, as_stream(stream)), fn);
 }
 
+size_t bt_quantize_weights_workspace_bytes(void) { return BT_WQ_WORKSPACE_BYTES; }
+
+bt_status bt_quantize_weights(const void *w, bt_dtype w_dtype, int64_t M, int64_t K,
+                              int scale_mode, float eps, uint8_t *packed, float *stats,
+                              void *workspace, size_t workspace_bytes, bt_stream stream) {
+    const char *fn = "bt_quantize_weights";
+    BT_TRY(check_mk(M, K, fn));
+    if (M > ((int64_t)1 << 31) / K)
+        return fail(BT_ERR_SHAPE, "%s: M*K=%lld exceeds 2^31", fn, (long long)(M * K));
+    if (w_dtype != BT_F32 && w_dtype != BT_BF16)
+        return fail(BT_ERR_DTYPE, "%s: w dtype must be BT_F32 or BT_BF16", fn);
+    if (scale_mode != BT_WSCALE_ABSMEAN && scale_mode != BT_WSCALE_ABSMAX)
+        return fail(BT_ERR_INVALID_ARG, "%s: unknown scale mode %d", fn, scale_mode);
+    if (!(eps >= 0.0f && eps <= 3.402823466e38f))
+        return fail(BT_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    BT_TRY(check_ptr(w, "w", fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (stats != nullptr && (reinterpret_cast<uintptr_t>(stats) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: stats is not 4-byte aligned", fn);
+    if (workspace == nullptr || workspace_bytes < BT_WQ_WORKSPACE_BYTES)
+        return fail(BT_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn,
+                    (size_t)BT_WQ_WORKSPACE_BYTES);
+    BT_TRY(check_ptr(workspace, "workspace", fn));
+    return hip_status(bt::launch_quantize_weights(w, w_dtype, M, K, scale_mode, eps, packed,
+                                                  stats, workspace, as_stream(stream)),
+                      fn);
+}
+
 bt_status bt_quant_act(const void *x, bt_dtype x_dtype, int64_t N, int64_t K, int8_t *xq,
                        float *x_scale, int32_t *x_sum, bt_stream stream) {
     const char *fn = "bt_quant_act";

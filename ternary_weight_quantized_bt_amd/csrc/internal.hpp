@@ -13,6 +13,10 @@ hipError_t launch_pack(const int8_t *w, int64_t M, int64_t K, float scale,
                        uint8_t *packed, int32_t *invalid, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int64_t M, int64_t K,
                          int8_t *w, hipStream_t s);
+// Float -> packed ternary weights (workspace: BT_WQ_WORKSPACE_BYTES).
+hipError_t launch_quantize_weights(const void *w, bt_dtype wdt, int64_t M, int64_t K, int mode,
+                                   float eps, uint8_t *packed, float *stats, void *workspace,
+                                   hipStream_t s);
 hipError_t launch_quant(const void *x, bt_dtype xdt, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t s);
 // Several inputs of N tokens each (widths K[i]) quantized in one launch.

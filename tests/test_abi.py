@@ -21,6 +21,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("bt_pack_ternary", "bt_unpack_ternary", "bt_quant_act",
+              "bt_quantize_weights", "bt_quantize_weights_workspace_bytes",
               "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
               "bt_layer_workspace_bytes", "bt_packed_bytes", "bt_last_error",
               "bt_abi_version"):
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 2
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 3
 
 
 def test_packed_bytes():
@@ -103,6 +104,36 @@ def test_quant_validation(args, status):
     with pytest.raises(bt.BtError) as e:
         bt.bt_quant_act(*args, stream=0)
     assert e.value.status == status
+
+
+WQ = bt.BT_WQ_WORKSPACE_BYTES
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, bt.BT_F32, 15, 256, 0, 0.0, A, None, A, WQ), bt.BT_ERR_SHAPE),
+    ((A, bt.BT_F32, 16, 200, 0, 0.0, A, None, A, WQ), bt.BT_ERR_SHAPE),
+    ((A, bt.BT_F32, 1 << 24, 256, 0, 0.0, A, None, A, WQ), bt.BT_ERR_SHAPE),  # M*K > 2^31
+    ((A, bt.BT_I32, 16, 256, 0, 0.0, A, None, A, WQ), bt.BT_ERR_DTYPE),
+    ((A, bt.BT_F32, 16, 256, 2, 0.0, A, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((A, bt.BT_F32, 16, 256, 0, -1e-5, A, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((A, bt.BT_F32, 16, 256, 0, float("nan"), A, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((A, bt.BT_F32, 16, 256, 0, float("inf"), A, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((None, bt.BT_F32, 16, 256, 0, 0.0, A, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((A, bt.BT_F32, 16, 256, 0, 0.0, None, None, A, WQ), bt.BT_ERR_INVALID_ARG),
+    ((A + 4, bt.BT_F32, 16, 256, 0, 0.0, A, None, A, WQ), bt.BT_ERR_ALIGN),
+    ((A, bt.BT_F32, 16, 256, 0, 0.0, A, A + 2, A, WQ), bt.BT_ERR_ALIGN),
+    ((A, bt.BT_F32, 16, 256, 0, 0.0, A, None, None, WQ), bt.BT_ERR_WORKSPACE),
+    ((A, bt.BT_F32, 16, 256, 0, 0.0, A, None, A, WQ - 1), bt.BT_ERR_WORKSPACE),
+    ((A, bt.BT_F32, 16, 256, 0, 0.0, A, None, A + 8, WQ), bt.BT_ERR_ALIGN),
+])
+def test_quantize_weights_validation(args, status):
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_quantize_weights(*args, stream=0)
+    assert e.value.status == status
+
+
+def test_quantize_weights_workspace_bytes():
+    assert bt.bt_quantize_weights_workspace_bytes() == WQ == 4096
 
 
 def _layer(shapes):

@@ -161,6 +161,52 @@ def ternary_weights(M: int, K: int, dist: str, seed: int,
     raise ValueError(dist)
 
 
+def float_weights(M: int, K: int, dist: str, seed: int, dtype: str = "f32",
+                  device="cpu") -> torch.Tensor:
+    """Float weights [M, K] (float32 or bfloat16) for the weight quantizer.
+
+    "normal":     N(0, 0.02^2), the spread of trained projection weights.
+    "student_t4": 0.02 * Student-t with 4 degrees of freedom (heavy tails).
+    "wide":       N(0, 1) * 2^u, u uniform on the integers [-130, 20]:
+                  magnitudes spread over ~150 binades, subnormals included.
+    "subnormal":  random float32 subnormal bit patterns with random signs.
+    "zeros":      all zero.
+    "ternarized": 0.0213 * t with t from ternary_weights(..., "p0_0.4"),
+                  a tensor already rounded to {-g, 0, +g}.
+    Values are drawn in float32 and cast (round to nearest) for bfloat16."""
+    g = _gen(seed, device)
+    if dist == "normal":
+        w = torch.randn((M, K), generator=g, device=device) * 0.02
+    elif dist == "student_t4":
+        z = torch.randn((M, K), generator=g, device=device)
+        chi2 = torch.zeros((M, K), device=device)
+        for _ in range(4):
+            e = torch.randn((M, K), generator=g, device=device)
+            chi2 += e * e
+        w = 0.02 * z / torch.sqrt(chi2 / 4.0)
+    elif dist == "wide":
+        z = torch.randn((M, K), generator=g, device=device)
+        u = torch.randint(-130, 21, (M, K), generator=g, device=device)
+        w = z * torch.exp2(u.to(torch.float32))
+    elif dist == "subnormal":
+        bits = torch.randint(0, 1 << 23, (M, K), generator=g, device=device,
+                             dtype=torch.int32)
+        sign = torch.randint(0, 2, (M, K), generator=g, device=device,
+                             dtype=torch.int32) << 31
+        w = (bits | sign).view(torch.float32)
+    elif dist == "zeros":
+        w = torch.zeros((M, K), device=device)
+    elif dist == "ternarized":
+        w = ternary_weights(M, K, "p0_0.4", seed, device).to(torch.float32) * 0.0213
+    else:
+        raise ValueError(dist)
+    if dtype == "f32":
+        return w.contiguous()
+    if dtype == "bf16":
+        return w.to(torch.bfloat16).contiguous()
+    raise ValueError(dtype)
+
+
 def activations(N: int, K: int, dist: str, seed: int, dtype: str,
                 outlier_frac: float = 0.0, outlier_scale: float = 1.0,
                 device="cpu") -> torch.Tensor:
