@@ -278,6 +278,40 @@ def prefill_extra(steps, warmup, use_graph):
     return res
 
 
+def weight_quant_extra(steps, warmup):
+    """The float -> ternary weight quantizer on one 28672 x 8192 bf16 matrix
+    (the gate / up shape of the 70B-class block), both scale modes.  Bytes
+    are those the passes must move: the weights read once per pass (max,
+    exact sum for AbsMean, pack) and the packed matrix written."""
+    import torch
+    import ternary_weight_quantized_bt_amd as bt
+    import workloads as W
+    M, K = 28672, 8192
+    dev = "cuda:0"
+    w = W.float_weights(M, K, "normal", 77, "bf16", device=dev)
+    packed = torch.empty(bt.bt_packed_bytes(M, K), dtype=torch.uint8, device=dev)
+    stats = torch.empty(2, dtype=torch.float32, device=dev)
+    wsb = bt.bt_quantize_weights_workspace_bytes()
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    res = {"shape": [M, K], "dtype": "bf16"}
+    for name, mode, passes in (("absmean", bt.BT_WSCALE_ABSMEAN, 3),
+                               ("absmax", bt.BT_WSCALE_ABSMAX, 2)):
+        def call():
+            bt.bt_quantize_weights(w, bt.BT_BF16, M, K, mode, 1e-5, packed, stats, ws, wsb)
+        for _ in range(warmup):
+            call()
+        t, _ = time_region(call, steps)
+        t /= steps
+        moved = passes * M * K * 2 + packed.numel()
+        res[name] = {"ms": round(t * 1e3, 4),
+                     "weights_gb_per_s": round(M * K * 2 / t / 1e9, 1),
+                     "moved_gb_per_s": round(moved / t / 1e9, 1),
+                     "frac_of_hbm_peak": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
+    del w, packed
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -391,6 +425,7 @@ def main():
         del model
         torch.cuda.empty_cache()
         extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
+        extra["weight_quantizer_70b_gate"] = weight_quant_extra(args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu:

@@ -22,12 +22,13 @@
 //   3. (AbsMean only) the exact sum.  With E the exponent of the max, a
 //      value m * 2^(e-150) (m the 24-bit significand, e the biased exponent,
 //      at least 1) with E - e < 32 adds m << (31 - (E - e)) -- at most 55
-//      bits -- to window 0, split into its two 32-bit halves so that no
-//      64-bit accumulator can overflow for up to 2^31 elements; E - e in
+//      bits -- to window 0, whose 64-bit sums are folded into 32-bit halves
+//      often enough that nothing can overflow below 2^31 elements; E - e in
 //      [32, 64) goes the same way to window 1; anything smaller (rare for
-//      weights) adds m to a per-exponent bin in LDS.  All sums are integers,
-//      so atomics in any order give the same totals;
-//   4. one thread turns the integers into s (a 384-bit sum divided by M*K
+//      weights: a wave checks each chunk and takes the window-0-only path
+//      when it can) adds m to a per-exponent bin in LDS.  All sums are
+//      integers, so atomics in any order give the same totals;
+//   4. one wave turns the integers into s (a 384-bit sum divided by M*K
 //      and rounded), d, and a float32 threshold t: since float32 division is
 //      correctly rounded and rounding is monotone, round(W / d) is +-1
 //      exactly when |W| > d * (0.5 + 2^-25) (the midpoint above 0.5); that
@@ -103,27 +104,48 @@ void wq_max_kernel(const T *__restrict__ w, int64_t chunks, WqState *st) {
     }
 }
 
-// Per-thread window sums (see the header): window 0 low / high halves,
-// window 1 low / high halves, in the order of WqState::win.
+// Low significand bits that are zero in every element of a T: a bfloat16
+// widened to float32 has 16.  Window terms are formed from m >> kZ, so the
+// totals carry the unit 2^kZ (the finalize adds it back).
+template <typename T> struct ZeroBits;
+template <> struct ZeroBits<float> { static constexpr int value = 0; };
+template <> struct ZeroBits<uint16_t> { static constexpr int value = 16; };
+
+// Totals of one thread, in the order of WqState::win: window 0 low / high
+// 32-bit halves, window 1 low / high halves.  Each window term is below
+// 2^(55 - kZ); terms are first summed in 64 bits (at most 2^(8 + kZ) of
+// them, so no overflow) and then folded into the halves, which cannot
+// overflow below 2^31 elements.
 struct WinAcc {
     unsigned long long v[4];
+    unsigned long long s0, s1;  // window sums since the last fold
+    __host__ __device__ void fold() {
+        v[0] += (uint32_t)s0;
+        v[1] += s0 >> 32;
+        v[2] += (uint32_t)s1;
+        v[3] += s1 >> 32;
+        s0 = s1 = 0;
+    }
 };
 
-// Adds |bits| to the windows; returns true (with the exponent e and the
-// significand m) when the value is too small for them and goes to a bin.
-__host__ __device__ inline bool accumulate(uint32_t bits, uint32_t E, WinAcc &acc,
-                                           uint32_t &e, uint32_t &m) {
+// Splits |bits| into significand m (hidden bit included) and exponent e
+// (at least 1: subnormals share exponent 1), value m * 2^(e - 150).
+__host__ __device__ inline void split(uint32_t bits, uint32_t &e, uint32_t &m) {
     const uint32_t a = bits & 0x7FFFFFFFu;
     const uint32_t ef = a >> 23;
     m = (a & 0x7FFFFFu) | (ef != 0u ? 0x800000u : 0u);
     e = ef > 1u ? ef : 1u;
-    const uint32_t dd = E - e;  // a <= max, so e <= E
-    const uint64_t v0 = dd < 32u ? (uint64_t)m << (31u - dd) : 0ull;
-    const uint64_t v1 = dd - 32u < 32u ? (uint64_t)m << (63u - dd) : 0ull;
-    acc.v[0] += (uint32_t)v0;
-    acc.v[1] += (uint32_t)(v0 >> 32);
-    acc.v[2] += (uint32_t)v1;
-    acc.v[3] += (uint32_t)(v1 >> 32);
+}
+
+// Any element: window 0 or 1, else (returns true) the per-exponent bin.
+template <int kZ>
+__host__ __device__ inline bool accumulate(uint32_t bits, uint32_t E, WinAcc &acc,
+                                           uint32_t &e, uint32_t &m) {
+    split(bits, e, m);
+    const uint32_t dd = E - e;  // |bits| <= max, so e <= E
+    const uint32_t mz = m >> kZ;
+    acc.s0 += dd < 32u ? (uint64_t)mz << (31u - dd) : 0ull;
+    acc.s1 += dd - 32u < 32u ? (uint64_t)mz << (63u - dd) : 0ull;
     return dd >= 64u && m != 0u;
 }
 
@@ -136,23 +158,51 @@ __device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
 template <typename T>
 __global__ __launch_bounds__(kWqThreads)
 void wq_sum_kernel(const T *__restrict__ w, int64_t chunks, WqState *st) {
+    constexpr int kZ = ZeroBits<T>::value;
+    constexpr int kFold = (1 << (8 + kZ)) / 8;  // chunks of 8 between folds
     __shared__ unsigned long long bins[256];
     __shared__ unsigned long long red[4][kWqWaves];
     for (int i = threadIdx.x; i < 256; i += kWqThreads) bins[i] = 0;
     __syncthreads();
-    // exponent field of the max, at least 1 (subnormals share exponent 1)
+    // exponent field of the max, at least 1
     const uint32_t E = max(__builtin_amdgcn_readfirstlane(st->max_bits) >> 23, 1u);
     WinAcc acc{};
+    int since = 0;
     for (int64_t c = (int64_t)blockIdx.x * kWqThreads + threadIdx.x; c < chunks;
          c += (int64_t)gridDim.x * kWqThreads) {
         uint32_t u[8];
         load_bits8(w + 8 * c, u);
+        // Common case, decided per wave: every nonzero element within 32
+        // binades of the max, so only window 0 is touched.
+        uint32_t far = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t e, m;
-            if (accumulate(u[i], E, acc, e, m)) atomicAdd(&bins[e], (unsigned long long)m);
+            split(u[i], e, m);
+            far |= (E - e >= 32u && m != 0u) ? 1u : 0u;
+        }
+        if (!__any((int)far)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t e, m;
+                split(u[i], e, m);
+                const uint32_t dd = min(E - e, 31u);  // zeros (m = 0) add 0
+                acc.s0 += (uint64_t)(m >> kZ) << (31u - dd);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t e, m;
+                if (accumulate<kZ>(u[i], E, acc, e, m))
+                    atomicAdd(&bins[e], (unsigned long long)m);
+            }
+        }
+        if (++since == kFold) {
+            acc.fold();
+            since = 0;
         }
     }
+    acc.fold();
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -170,75 +220,101 @@ void wq_sum_kernel(const T *__restrict__ w, int64_t chunks, WqState *st) {
         if (bins[i] != 0) atomicAdd(&st->bins[i], bins[i]);
 }
 
-// 384-bit unsigned integer, 32-bit limbs, least significant first.
+// 384-bit unsigned integer, 32-bit limbs, least significant first.  Every
+// loop is unrolled over the limbs with compares instead of indexing, so the
+// limbs stay in registers.
 constexpr int kLimbs = 12;
 
+// x += v * 2^shift (0 <= shift, and the sum fits).
 __host__ __device__ inline void big_add(uint32_t (&x)[kLimbs], unsigned long long v, int shift) {
-    int j = shift >> 5;
-    const int r = shift & 31;
-    // v << r spans up to three limbs
-    unsigned long long lo = v << r;
-    unsigned long long hi = r ? (v >> (64 - r)) : 0ull;
-    const uint32_t part[3] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi};
+    const int j = shift >> 5, r = shift & 31;
+    const unsigned long long lo = v << r;
+    const uint32_t p0 = (uint32_t)lo, p1 = (uint32_t)(lo >> 32);
+    const uint32_t p2 = r ? (uint32_t)(v >> (64 - r)) : 0u;
     unsigned long long carry = 0;
-    for (int k = 0; j + k < kLimbs; ++k) {
-        const unsigned long long add = (k < 3 ? part[k] : 0u);
-        if (k >= 3 && carry == 0) break;
-        const unsigned long long t = (unsigned long long)x[j + k] + add + carry;
-        x[j + k] = (uint32_t)t;
+#pragma unroll
+    for (int k = 0; k < kLimbs; ++k) {
+        const uint32_t add = k == j ? p0 : (k == j + 1 ? p1 : (k == j + 2 ? p2 : 0u));
+        const unsigned long long t = (unsigned long long)x[k] + add + carry;
+        x[k] = (uint32_t)t;
         carry = t >> 32;
     }
 }
 
-__host__ __device__ inline int big_bits(const uint32_t (&x)[kLimbs]) {  // bit length
-    for (int j = kLimbs - 1; j >= 0; --j)
-        if (x[j] != 0u) return 32 * j + 32 - __builtin_clz(x[j]);
-    return 0;
+__host__ __device__ inline uint32_t big_limb(const uint32_t (&x)[kLimbs], int j) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = 0; k < kLimbs; ++k) v = k == j ? x[k] : v;
+    return v;
 }
 
-__host__ __device__ inline uint32_t big_bit(const uint32_t (&x)[kLimbs], int i) {
-    return (i >= 0 && i < 32 * kLimbs) ? (x[i >> 5] >> (i & 31)) & 1u : 0u;
+__host__ __device__ inline int big_bits(const uint32_t (&x)[kLimbs]) {  // bit length
+    int b = 0;
+#pragma unroll
+    for (int k = 0; k < kLimbs; ++k) b = x[k] != 0u ? 32 * k + 32 - __builtin_clz(x[k]) : b;
+    return b;
 }
 
 __host__ __device__ inline bool big_any_below(const uint32_t (&x)[kLimbs], int i) {  // bits [0, i)
-    for (int j = 0; j < kLimbs && 32 * j < i; ++j) {
-        const int n = i - 32 * j < 32 ? i - 32 * j : 32;
-        const uint32_t mask = n == 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
-        if (x[j] & mask) return true;
+    uint32_t any = 0;
+#pragma unroll
+    for (int k = 0; k < kLimbs; ++k) {
+        const int n = i - 32 * k;
+        const uint32_t mask = n >= 32 ? 0xFFFFFFFFu : (n > 0 ? (1u << n) - 1u : 0u);
+        any |= x[k] & mask;
     }
-    return false;
+    return any != 0u;
 }
 
-// The mean, rounded once: sum = X * 2^B, mean = X / n * 2^B.
-__host__ __device__ inline float exact_mean(const WqState *st, int64_t n) {
+// The exact mean, in three steps: X = the windows' totals in units of 2^B
+// (mean_begin), plus each bin (mean_add_bin), then X / n rounded once
+// (mean_round).  B = min(E - 213, -149) lies at or below every unit used.
+struct ExactSum {
+    uint32_t x[kLimbs];
+    int B;
+};
+
+__host__ __device__ inline void mean_begin(ExactSum &S, const WqState *st, int kZ) {
     const int E = st->max_bits >> 23 > 1u ? (int)(st->max_bits >> 23) : 1;
-    const int B = E - 213 < -149 ? E - 213 : -149;  // unit of the least significant bit of X
-    uint32_t x[kLimbs] = {};
-    big_add(x, st->win[0], E - 181 - B);
-    big_add(x, st->win[1], E - 181 + 32 - B);
-    big_add(x, st->win[2], E - 213 - B);
-    big_add(x, st->win[3], E - 213 + 32 - B);
-    for (int e = 1; e < 256; ++e)
-        if (st->bins[e] != 0) big_add(x, st->bins[e], e - 150 - B);
-    // Q = X / n, R = X % n (n < 2^32)
+    S.B = E - 213 < -149 ? E - 213 : -149;
+#pragma unroll
+    for (int k = 0; k < kLimbs; ++k) S.x[k] = 0u;
+    big_add(S.x, st->win[0], E - 181 + kZ - S.B);       // window 0, low halves
+    big_add(S.x, st->win[1], E - 181 + kZ + 32 - S.B);  // window 0, high halves
+    big_add(S.x, st->win[2], E - 213 + kZ - S.B);       // window 1, low halves
+    big_add(S.x, st->win[3], E - 213 + kZ + 32 - S.B);  // window 1, high halves
+}
+
+// Significand sum v of exponent e (e >= 1): v * 2^(e - 150).
+__host__ __device__ inline void mean_add_bin(ExactSum &S, int e, unsigned long long v) {
+    big_add(S.x, v, e - 150 - S.B);
+}
+
+__host__ __device__ inline float mean_round(ExactSum &S, int64_t n) {
+    uint32_t (&x)[kLimbs] = S.x;
+    const int B = S.B;
+    // Q = X / n, R = X % n (n < 2^32, so every step fits 64 bits)
     const unsigned long long nn = (unsigned long long)n;
     unsigned long long rem = 0;
-    for (int j = kLimbs - 1; j >= 0; --j) {
-        const unsigned long long cur = (rem << 32) | x[j];
-        x[j] = (uint32_t)(cur / nn);
+#pragma unroll
+    for (int k = kLimbs - 1; k >= 0; --k) {
+        const unsigned long long cur = (rem << 32) | x[k];
+        x[k] = (uint32_t)(cur / nn);
         rem = cur % nn;
     }
     // keep 24 significant bits, or the bits down to 2^-149
-    const int p = big_bits(x) - 1;                 // -1 when Q == 0
+    const int p = big_bits(x) - 1;                        // -1 when Q == 0
     const int q = p + B - 23 > -149 ? p + B - 23 : -149;  // exponent of the last kept bit
-    const int k = q - B;                            // bits of Q dropped (B <= -149 <= q)
-    uint32_t m = 0;
-    for (int i = 0; i < 25; ++i) m |= big_bit(x, k + i) << i;
+    const int k = q - B;                                   // bits of Q dropped (B <= -149 <= q)
+    // bits [k, k + 25) of Q through a 64-bit window (k % 32 + 25 <= 56)
+    const unsigned long long win =
+        (unsigned long long)big_limb(x, k >> 5) | ((unsigned long long)big_limb(x, (k >> 5) + 1) << 32);
+    uint32_t m = (uint32_t)(win >> (k & 31)) & 0x1FFFFFFu;
     bool up;
     if (k == 0) {
         up = 2 * rem > nn || (2 * rem == nn && (m & 1u));
     } else {
-        const bool half = big_bit(x, k - 1) != 0u;
+        const bool half = ((big_limb(x, (k - 1) >> 5) >> ((k - 1) & 31)) & 1u) != 0u;
         const bool sticky = big_any_below(x, k - 1) || rem != 0;
         up = half && (sticky || (m & 1u));
     }
@@ -256,16 +332,40 @@ __host__ __device__ inline uint32_t code_threshold(float d) {
     return (double)t32 <= t ? tb + 1u : tb;
 }
 
-__global__ void wq_finalize_kernel(WqState *st, int64_t n, int mode, float eps, float *stats) {
-    if (threadIdx.x != 0) return;
-    const float s = mode == BT_WSCALE_ABSMAX ? __uint_as_float(st->max_bits) : exact_mean(st, n);
+// One wave: lanes load the 256 bins in parallel, the nonzero ones are
+// added one at a time (wave-uniform), every lane computing the same result.
+__global__ __launch_bounds__(kWave)
+void wq_finalize_kernel(WqState *st, int64_t n, int mode, int kZ, float eps, float *stats) {
+    const int lane = threadIdx.x;
+    float s;
+    if (mode == BT_WSCALE_ABSMAX) {
+        s = __uint_as_float(st->max_bits);
+    } else {
+        ExactSum S;
+        mean_begin(S, st, kZ);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned long long b = st->bins[4 * lane + i];
+            unsigned long long mask = __ballot(b != 0ull);
+            while (mask != 0ull) {
+                const int l = __ffsll((long long)mask) - 1;
+                mask &= mask - 1ull;
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+                mean_add_bin(S, 4 * l + i, ((unsigned long long)hi << 32) | lo);
+            }
+        }
+        s = mean_round(S, n);
+    }
     const float d = __fadd_rn(s, eps);
-    st->s = s;
-    st->d = d;
-    st->thr_bits = code_threshold(d);
-    if (stats != nullptr) {
-        stats[0] = s;
-        stats[1] = d;
+    if (lane == 0) {
+        st->s = s;
+        st->d = d;
+        st->thr_bits = code_threshold(d);
+        if (stats != nullptr) {
+            stats[0] = s;
+            stats[1] = d;
+        }
     }
 }
 
@@ -329,7 +429,8 @@ hipError_t launch_wq_t(const T *w, int64_t M, int64_t K, int mode, float eps,
     hipLaunchKernelGGL((wq_max_kernel<T>), dim3(grid), dim3(kWqThreads), 0, s, w, chunks, st);
     if (mode == BT_WSCALE_ABSMEAN)
         hipLaunchKernelGGL((wq_sum_kernel<T>), dim3(grid), dim3(kWqThreads), 0, s, w, chunks, st);
-    hipLaunchKernelGGL(wq_finalize_kernel, dim3(1), dim3(kWave), 0, s, st, n, mode, eps, stats);
+    hipLaunchKernelGGL(wq_finalize_kernel, dim3(1), dim3(kWave), 0, s, st, n, mode,
+                       ZeroBits<T>::value, eps, stats);
     const int64_t nslots = (M / kTileRows) * (K / kTileCols) * kWave;
     const int64_t blocks = (nslots + kWqThreads - 1) / kWqThreads;
     hipLaunchKernelGGL((wq_pack_kernel<T>), dim3((unsigned)blocks), dim3(kWqThreads), 0, s,
