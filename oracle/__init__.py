@@ -9,7 +9,8 @@ element at a time); this module only builds it with gcc and passes numpy
 arrays through ctypes.  The readings of the pages it follows are listed in the
 header of that file.  The float -> ternary weight quantizer (AbsMean and
 max|w| scales, RoundClip) is ``weight_quant.py``: numpy plus exact Python
-integer arithmetic, its readings in its own header.
+integer arithmetic, its readings in its own header.  Dequantization
+(to_float) and the I2_S byte layout are ``interop.py`` (numpy).
 
 Sources, cited by page title and section:
   [I2S]  "How BitNet's 1-Bit (I2_S) Quantization Works Compared to Standard
