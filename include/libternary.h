@@ -20,6 +20,7 @@
  *   [PARA] "LLM Quantization Paradigms: FP8, AWQ, EXL2 & BitNet b1.58 in 2026"
  *   [PREP] "BitNet Inference Preprocessing: Converting Hugging Face
  *          Checkpoints to I2S GGUF"
+ *   [IK]   "ik_llama.cpp 运行 BitNet b1.58 2B 模型实战…"
  *
  * Conventions for every entry point:
  *   - Matrices are row-major.  W is [M, K] = [out, in]; x is [N, K]; y is
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 3
+#define BT_ABI_VERSION 4
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -149,6 +150,42 @@ bt_status bt_quantize_weights(const void *w, bt_dtype w_dtype, int64_t M, int64_
                               int scale_mode, float eps, uint8_t *packed,
                               float *stats, void *workspace,
                               size_t workspace_bytes, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Dequantization (to_float) and the I2_S byte layout.
+ * ([IK] section 5.1: an I2_S tensor is dequantized to float32 as a whole
+ * before requantization; [I2S] "Ternary Representation and Packing" and
+ * "Per-Tensor Scaling Strategy": codes 0/1/2 shifted left by 6 - 2 * group
+ * in blocks of QK_I2_S weights, one float scale after the codes.)
+ *
+ * bt_dequantize_weights: w[m,k] = (code - 1) * scale as a float32 product
+ *   (exact: -scale, a signed zero or scale), written as float32, or rounded
+ *   to nearest even for BT_BF16.  w is [M, K] row-major.
+ *
+ * I2_S layout, as read here (the pages do not give QK_I2_S, so it is the
+ * caller's `block`: a positive multiple of 4 that divides M*K):
+ *   the M*K weights in row-major order are cut into blocks of `block`;
+ *   weight j of a block has group g = j / (block/4) and lies in byte
+ *   j % (block/4) of the block's block/4 bytes, at bits [7-2g : 6-2g];
+ *   the float32 scale follows the M*K/4 code bytes (bt_i2s_bytes(M, K) =
+ *   M*K/4 + 4 bytes in all).
+ * bt_i2s_import: I2_S bytes -> T16Q256 packed bytes with the same scale.
+ *   Code 3 is stored as 2 (+1) and, if invalid_count is not NULL, ADDED to
+ *   *invalid_count (a device int32), as bt_pack_ternary does.
+ * bt_i2s_export: T16Q256 packed bytes -> I2_S bytes.
+ * Shapes as for bt_pack_ternary; buffers are device memory, 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t bt_i2s_bytes(int64_t M, int64_t K);
+
+bt_status bt_dequantize_weights(const uint8_t *packed, int64_t M, int64_t K,
+                                void *w, bt_dtype w_dtype, bt_stream stream);
+
+bt_status bt_i2s_import(const uint8_t *i2s, int64_t M, int64_t K, int64_t block,
+                        uint8_t *packed, int32_t *invalid_count,
+                        bt_stream stream);
+
+bt_status bt_i2s_export(const uint8_t *packed, int64_t M, int64_t K,
+                        int64_t block, uint8_t *i2s, bt_stream stream);
 
 /* ------------------------------------------------------------------------
  * Per-token absmax int8 activation quantization ([PARA] section 5, Quant8).

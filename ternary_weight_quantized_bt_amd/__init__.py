@@ -83,7 +83,7 @@ BT_WSCALE_ABSMAX = 1
 BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 
@@ -113,6 +113,14 @@ def lib() -> ctypes.CDLL:
         L.bt_pack_ternary.restype = S
         L.bt_unpack_ternary.argtypes = [P, I64, I64, P, P]
         L.bt_unpack_ternary.restype = S
+        L.bt_i2s_bytes.argtypes = [I64, I64]
+        L.bt_i2s_bytes.restype = ctypes.c_size_t
+        L.bt_dequantize_weights.argtypes = [P, I64, I64, P, S, P]
+        L.bt_dequantize_weights.restype = S
+        L.bt_i2s_import.argtypes = [P, I64, I64, I64, P, P, P]
+        L.bt_i2s_import.restype = S
+        L.bt_i2s_export.argtypes = [P, I64, I64, I64, P, P]
+        L.bt_i2s_export.restype = S
         L.bt_quantize_weights_workspace_bytes.argtypes = []
         L.bt_quantize_weights_workspace_bytes.restype = ctypes.c_size_t
         L.bt_quantize_weights.argtypes = [P, S, I64, I64, S, ctypes.c_float, P, P, P,
@@ -188,6 +196,23 @@ def bt_unpack_ternary(packed, M, K, w, stream=None):
     _check(lib().bt_unpack_ternary(_p(packed), M, K, _p(w), _stream(stream)))
 
 
+def bt_i2s_bytes(M: int, K: int) -> int:
+    return lib().bt_i2s_bytes(M, K)
+
+
+def bt_dequantize_weights(packed, M, K, w, w_dtype, stream=None):
+    _check(lib().bt_dequantize_weights(_p(packed), M, K, _p(w), w_dtype, _stream(stream)))
+
+
+def bt_i2s_import(i2s, M, K, block, packed, invalid_count=None, stream=None):
+    _check(lib().bt_i2s_import(_p(i2s), M, K, block, _p(packed), _p(invalid_count),
+                               _stream(stream)))
+
+
+def bt_i2s_export(packed, M, K, block, i2s, stream=None):
+    _check(lib().bt_i2s_export(_p(packed), M, K, block, _p(i2s), _stream(stream)))
+
+
 def bt_quantize_weights_workspace_bytes() -> int:
     return lib().bt_quantize_weights_workspace_bytes()
 
@@ -261,6 +286,35 @@ def unpack(packed: torch.Tensor, M: int, K: int, stream=None):
     w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
     bt_unpack_ternary(packed, M, K, w, stream)
     return w
+
+
+def dequantize(packed: torch.Tensor, M: int, K: int, dtype=torch.float32, stream=None):
+    """Packed weights -> float32 / bfloat16 [M, K] device tensor
+    ((code - 1) * scale)."""
+    w = torch.empty((M, K), dtype=dtype, device=packed.device)
+    bt_dequantize_weights(packed, M, K, w, _BT_DTYPE[dtype], stream)
+    return w
+
+
+def i2s_import(i2s: torch.Tensor, M: int, K: int, block: int, invalid_count=None,
+               stream=None):
+    """I2_S bytes (blocks of `block` weights) -> packed T16Q256 tensor."""
+    n = bt_packed_bytes(M, K)
+    if n == 0:
+        raise BtError(BT_ERR_SHAPE, bt_last_error())
+    packed = torch.empty(n, dtype=torch.uint8, device=i2s.device)
+    bt_i2s_import(i2s, M, K, block, packed, invalid_count, stream)
+    return packed
+
+
+def i2s_export(packed: torch.Tensor, M: int, K: int, block: int, stream=None):
+    """Packed T16Q256 tensor -> I2_S bytes (blocks of `block` weights)."""
+    n = bt_i2s_bytes(M, K)
+    if n == 0:
+        raise BtError(BT_ERR_SHAPE, bt_last_error())
+    out = torch.empty(n, dtype=torch.uint8, device=packed.device)
+    bt_i2s_export(packed, M, K, block, out, stream)
+    return out
 
 
 def quantize_weights(w: torch.Tensor, mode: str = "absmean", eps: float = 0.0,

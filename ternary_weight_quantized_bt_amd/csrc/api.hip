@@ -167,6 +167,52 @@ bt_status bt_unpack_ternary(const uint8_t *packed, int64_t M, int64_t K, int8_t 
     return hip_status(bt::launch_unpack(packed, M, K, w, as_stream(stream)), fn);
 }
 
+size_t bt_i2s_bytes(int64_t M, int64_t K) {
+    if (check_mk(M, K, "bt_i2s_bytes") != BT_OK) return 0;
+    return (size_t)(M * K / 4) + 4;
+}
+
+bt_status bt_dequantize_weights(const uint8_t *packed, int64_t M, int64_t K, void *w,
+                                bt_dtype w_dtype, bt_stream stream) {
+    const char *fn = "bt_dequantize_weights";
+    BT_TRY(check_mk(M, K, fn));
+    if (w_dtype != BT_F32 && w_dtype != BT_BF16)
+        return fail(BT_ERR_DTYPE, "%s: w dtype must be BT_F32 or BT_BF16", fn);
+    BT_TRY(check_ptr(packed, "packed", fn));
+    BT_TRY(check_ptr(w, "w", fn));
+    return hip_status(bt::launch_dequant(packed, M, K, w, w_dtype, as_stream(stream)), fn);
+}
+
+static bt_status check_i2s_block(int64_t M, int64_t K, int64_t block, const char *fn) {
+    if (block <= 0 || block % 4 != 0 || block > ((int64_t)1 << 31) || (M * K) % block != 0)
+        return fail(BT_ERR_SHAPE, "%s: block=%lld must be a positive multiple of 4 dividing M*K",
+                    fn, (long long)block);
+    return BT_OK;
+}
+
+bt_status bt_i2s_import(const uint8_t *i2s, int64_t M, int64_t K, int64_t block,
+                        uint8_t *packed, int32_t *invalid_count, bt_stream stream) {
+    const char *fn = "bt_i2s_import";
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_i2s_block(M, K, block, fn));
+    BT_TRY(check_ptr(i2s, "i2s", fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (invalid_count != nullptr && (reinterpret_cast<uintptr_t>(invalid_count) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: invalid_count is not 4-byte aligned", fn);
+    return hip_status(
+        bt::launch_i2s_import(i2s, M, K, block, packed, invalid_count, as_stream(stream)), fn);
+}
+
+bt_status bt_i2s_export(const uint8_t *packed, int64_t M, int64_t K, int64_t block,
+                        uint8_t *i2s, bt_stream stream) {
+    const char *fn = "bt_i2s_export";
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_i2s_block(M, K, block, fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    BT_TRY(check_ptr(i2s, "i2s", fn));
+    return hip_status(bt::launch_i2s_export(packed, M, K, block, i2s, as_stream(stream)), fn);
+}
+
 size_t bt_quantize_weights_workspace_bytes(void) { return BT_WQ_WORKSPACE_BYTES; }
 
 bt_status bt_quantize_weights(const void *w, bt_dtype w_dtype, int64_t M, int64_t K,

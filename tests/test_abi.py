@@ -22,6 +22,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("bt_pack_ternary", "bt_unpack_ternary", "bt_quant_act",
               "bt_quantize_weights", "bt_quantize_weights_workspace_bytes",
+              "bt_dequantize_weights", "bt_i2s_import", "bt_i2s_export", "bt_i2s_bytes",
               "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
               "bt_layer_workspace_bytes", "bt_packed_bytes", "bt_last_error",
               "bt_abi_version"):
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 3
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 4
 
 
 def test_packed_bytes():
@@ -134,6 +135,31 @@ def test_quantize_weights_validation(args, status):
 
 def test_quantize_weights_workspace_bytes():
     assert bt.bt_quantize_weights_workspace_bytes() == WQ == 4096
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    ("bt_dequantize_weights", (A, 16, 256, A, bt.BT_I32), bt.BT_ERR_DTYPE),
+    ("bt_dequantize_weights", (A, 15, 256, A, bt.BT_F32), bt.BT_ERR_SHAPE),
+    ("bt_dequantize_weights", (None, 16, 256, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ("bt_dequantize_weights", (A, 16, 256, A + 2, bt.BT_BF16), bt.BT_ERR_ALIGN),
+    ("bt_i2s_import", (A, 16, 256, 6, A), bt.BT_ERR_SHAPE),
+    ("bt_i2s_import", (A, 16, 256, 0, A), bt.BT_ERR_SHAPE),
+    ("bt_i2s_import", (A, 16, 256, 3 * 256, A), bt.BT_ERR_SHAPE),  # does not divide M*K
+    ("bt_i2s_import", (A, 16, 256, 128, None), bt.BT_ERR_INVALID_ARG),
+    ("bt_i2s_import", (A + 1, 16, 256, 128, A), bt.BT_ERR_ALIGN),
+    ("bt_i2s_export", (A, 16, 256, -4, A), bt.BT_ERR_SHAPE),
+    ("bt_i2s_export", (A, 16, 200, 4, A), bt.BT_ERR_SHAPE),
+    ("bt_i2s_export", (A, 16, 256, 4, None), bt.BT_ERR_INVALID_ARG),
+])
+def test_interop_validation(fn, args, status):
+    with pytest.raises(bt.BtError) as e:
+        getattr(bt, fn)(*args, stream=0)
+    assert e.value.status == status
+
+
+def test_i2s_bytes():
+    assert bt.bt_i2s_bytes(16, 256) == 16 * 256 // 4 + 4
+    assert bt.bt_i2s_bytes(16, 100) == 0
 
 
 def _layer(shapes):
