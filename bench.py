@@ -70,6 +70,11 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB, five times "
                          "(reference for the HBM traffic counters)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
+                    help="no GPU: read four rocprofv3 --pmc output folders (copy "
+                         "FETCH_SIZE, copy WRITE_SIZE, step FETCH_SIZE, step "
+                         "WRITE_SIZE) and rewrite the layer kernel's entry of "
+                         "profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -219,6 +224,69 @@ def read_traffic(kernel_name, sha):
     return e.get("bytes_per_launch")
 
 
+def _pmc_rows(folder, counter):
+    """(kernel name, counter value) of every dispatch in a rocprofv3 --pmc
+    csv output folder."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "*counter_collection.csv")):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(copy_fetch, copy_write, k_fetch, k_write):
+    """HBM bytes per launch of the layer kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for a 1 GiB
+    device copy (the copy reads and writes 2^30 bytes)."""
+    name = "layer_dot4_kernel"
+    copy = (1 << 30) / 1024.0
+
+    def mean(rows, key):
+        v = [x for k, x in rows if key in k]
+        if not v:
+            raise SystemExit(f"no {key} dispatches found")
+        return sum(v) / len(v), len(v)
+
+    cf, _ = mean(_pmc_rows(copy_fetch, "FETCH_SIZE"), "copyBuffer")
+    cw, _ = mean(_pmc_rows(copy_write, "WRITE_SIZE"), "copyBuffer")
+    kf, n = mean(_pmc_rows(k_fetch, "FETCH_SIZE"), name)
+    kw, _ = mean(_pmc_rows(k_write, "WRITE_SIZE"), name)
+    rf, rw = copy / cf, copy / cw
+    read, write = kf * 1024 * rf, kw * 1024 * rw
+    alg = _block_packed_bytes()
+    entry = {
+        "kernel_sha": kernel_sha(name),
+        "bytes_per_launch": int(round(read + write)),
+        "read_bytes_per_launch": int(round(read)),
+        "write_bytes_per_launch": int(round(write)),
+        "algorithmic_bytes_per_launch": alg,
+        "read_over_algorithmic": round(read / alg, 4),
+        "calibration": f"1 GiB device copy: FETCH_SIZE {cf:.1f} KiB (read factor {rf:.5f}), "
+                       f"WRITE_SIZE {cw:.0f} KiB (write factor {rw:.4f})",
+        "workload": "stream70b, 1 token, one launch per layer",
+        "dispatches": n,
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        d = {}
+    d[name] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(entry, indent=1))
+
+
+def _block_packed_bytes():
+    """Packed code bytes of one 70B-class block (the seven projections)."""
+    import workloads as W
+    return W.STREAM70B.packed_bytes_per_layer
+
+
 def cpu_baseline(wl, N, budget_s):
     """The oracle on layer 0 of the workload (all seven projections, the same
     seeded weights and inputs), repeated until the time budget is used."""
@@ -314,6 +382,9 @@ def weight_quant_extra(steps, warmup):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path", file=sys.stderr)
