@@ -391,8 +391,10 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
     // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
     static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
     static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
+    bt::Group groups[BT_LAYER_INPUTS];
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
-        bt::Group g{};
+        bt::Group &g = groups[i];
+        g = bt::Group{};
         g.count = kCount[i];
         for (int j = 0; j < g.count; ++j) {
             const int p = kFirst[i] + j;
@@ -404,6 +406,14 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         g.xsum = ws.xsum[i];
         g.N = N;
         g.ydt = io->y_dtype;
+    }
+    if (quantized && N > bt::kDot4MaxN && N < BT_PREFILL_MIN_N) {
+        // matrix-core decode: the four groups side by side in one launch
+        const hipError_t e = bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s);
+        return e == hipSuccess ? ok() : hip_status(e, fn);
+    }
+    for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+        const bt::Group &g = groups[i];
         hipError_t e;
         if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, Kin[i], io->x_dtype)) {
             // one launch: the decode kernel quantizes its input itself

@@ -62,6 +62,10 @@ hipError_t launch_decode(const Group &g, hipStream_t s);
 // prologue (x is the float / bf16 input of the group).  Only for shapes where
 // decode_fuses_quant(N, K) holds.
 bool decode_fuses_quant(int64_t N, int64_t K, bt_dtype xdt);
+// Matrix-core decode (kDot4MaxN < N < BT_PREFILL_MIN_N) of up to four groups,
+// each with its own quantized input, in one launch; results equal
+// launch_decode per group.
+hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s);
 hipError_t launch_decode_fused(const Group &g, const void *x, bt_dtype xdt, hipStream_t s);
 // Prefill path: tiled int8 matrix-core product.
 hipError_t launch_prefill(const Group &g, hipStream_t s);

@@ -74,9 +74,11 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0
 // (rows nb * 256 bytes apart); when there is more than one phase, per-tile
 // int32 partial sums carry over in LDS, after the codes, from one phase to
 // the next, and the last phase dequantizes and stores.
+// One group's work; the workgroup is number bx of the gx that run this group
+// (blockIdx.x and gridDim.x of a launch for this group alone).
 template <int WAVES, int P, int RING>
-__global__ __launch_bounds__(WAVES * kWave)
-void decode_mfma_kernel(GroupArgs a, int nph, int qph) {
+__device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph, int64_t bx,
+                                           int64_t gx) {
     static_assert(WAVES % P == 0, "K split must divide the waves");
     constexpr int TPW = WAVES / P;  // tiles per workgroup iteration
     static_assert(RING <= 63, "wait count exceeds the counter");
@@ -96,8 +98,8 @@ void decode_mfma_kernel(GroupArgs a, int nph, int qph) {
     const int kpart = wave % P, sub = wave / P;
     const int64_t total = group_tiles(a);
     const int64_t ngroups = (total + TPW - 1) / TPW;
-    const int64_t nit = (ngroups - blockIdx.x + gridDim.x - 1) / gridDim.x;
-    auto tile_of = [&](int64_t it) { return (blockIdx.x + it * gridDim.x) * TPW + sub; };
+    const int64_t nit = (ngroups - bx + gx - 1) / gx;
+    auto tile_of = [&](int64_t it) { return (bx + it * gx) * TPW + sub; };
     // partial sums: after the codes of the largest phase (16-row allocation)
     const int64_t rows_alloc = min((int64_t)16, a.N);
     v4i *const part = reinterpret_cast<v4i *>(
@@ -266,6 +268,37 @@ void decode_mfma_kernel(GroupArgs a, int nph, int qph) {
     }
 }
 
+template <int WAVES, int P, int RING>
+__global__ __launch_bounds__(WAVES * kWave)
+void decode_mfma_kernel(GroupArgs a, int nph, int qph) {
+    mfma_group<WAVES, P, RING>(a, nph, qph, blockIdx.x, gridDim.x);
+}
+
+// Up to four groups (a block's q/k/v, o, gate/up and down, each with its own
+// input) in one grid: workgroups [start[i], start[i+1]) run group i.  Each
+// branch is the whole single-group body on a fixed argument block, so
+// nothing is indexed dynamically.
+constexpr int kMaxMulti = 4;
+struct MultiArgs {
+    GroupArgs g[kMaxMulti];
+    int nph[kMaxMulti], qph[kMaxMulti];
+    int start[kMaxMulti + 1];  // unused groups have empty ranges
+};
+
+template <int WAVES, int P, int RING>
+__global__ __launch_bounds__(WAVES * kWave)
+void decode_mfma_multi_kernel(MultiArgs m) {
+    const int b = (int)blockIdx.x;
+    if (b < m.start[1])
+        mfma_group<WAVES, P, RING>(m.g[0], m.nph[0], m.qph[0], b, m.start[1]);
+    else if (b < m.start[2])
+        mfma_group<WAVES, P, RING>(m.g[1], m.nph[1], m.qph[1], b - m.start[1], m.start[2] - m.start[1]);
+    else if (b < m.start[3])
+        mfma_group<WAVES, P, RING>(m.g[2], m.nph[2], m.qph[2], b - m.start[2], m.start[3] - m.start[2]);
+    else
+        mfma_group<WAVES, P, RING>(m.g[3], m.nph[3], m.qph[3], b - m.start[3], m.start[4] - m.start[3]);
+}
+
 hipError_t launch_mf(const GroupArgs &a, int nph, int qph, int64_t grid, size_t shmem,
                      hipStream_t s) {
     auto kern = decode_mfma_kernel<kMfWaves, kMfSplit, kMfRing>;
@@ -281,33 +314,107 @@ hipError_t launch_mf(const GroupArgs &a, int nph, int qph, int64_t grid, size_t 
     return hipGetLastError();
 }
 
+// K phases of a group: as few as keep one phase's codes within kMfCodesMax.
+struct Plan {
+    int64_t nph, qph, codes, groups;
+};
+Plan plan_group(const GroupArgs &a) {
+    constexpr int TPW = kMfWaves / kMfSplit;
+    Plan p;
+    const int64_t rows = min((int64_t)16, a.N);
+    const int64_t qb = a.K / kTileCols;
+    const int64_t per_block = rows * kTileCols;
+    const int64_t max_blocks = max((int64_t)1, kMfCodesMax / per_block);
+    p.nph = (qb + max_blocks - 1) / max_blocks;
+    p.qph = (qb + p.nph - 1) / p.nph;
+    p.codes = (rows * p.qph * kTileCols + 1023) / 1024 * 1024;
+    p.groups = (group_tiles(a) + TPW - 1) / TPW;
+    return p;
+}
+
+// With more than one phase, at most kMfPhaseTiles iterations per workgroup
+// keep their partial sums: the grid is at least groups / kMfPhaseTiles, and
+// the partial sums take nit_max KiB per tile of an iteration.
+int64_t phase_grid(const Plan &p, int64_t grid) {
+    return p.nph > 1 ? max(grid, (p.groups + kMfPhaseTiles - 1) / kMfPhaseTiles) : grid;
+}
+int64_t partial_bytes(const Plan &p, int64_t grid) {
+    constexpr int TPW = kMfWaves / kMfSplit;
+    if (p.nph <= 1) return 0;
+    return (p.groups + grid - 1) / grid * TPW * kWave * 16;
+}
+
+// static LDS: partial sums of the waves (2 x 7 KiB) and the token table
+constexpr int64_t kMfFixedLds = 2 * (kMfSplit - 1) * kWave * 16 + 256;
+
 }  // namespace
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     if (a.N <= 0 || group_tiles(a) == 0) return hipSuccess;
-    constexpr int TPW = kMfWaves / kMfSplit;
-    const int64_t rows = min((int64_t)16, a.N);
-    const int64_t qb = a.K / kTileCols;
-    // phases: as few as keep one phase's codes within kMfCodesMax
-    const int64_t per_block = rows * kTileCols;
-    const int64_t max_blocks = max((int64_t)1, kMfCodesMax / per_block);
-    const int64_t nph = (qb + max_blocks - 1) / max_blocks;
-    const int64_t qph = (qb + nph - 1) / nph;
-    const int64_t codes = (rows * qph * kTileCols + 1023) / 1024 * 1024;
-    // static LDS: partial sums of the waves (2 x 7 KiB) and the token table
-    const int64_t fixed = 2 * (kMfSplit - 1) * kWave * 16 + 256;
+    const Plan p = plan_group(a);
     const int64_t tgroups = (a.N + 15) / 16;
-    const int64_t groups = (group_tiles(a) + TPW - 1) / TPW;
-    int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (codes + fixed)));
-    int64_t grid = max((int64_t)1, min(groups, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups));
-    int64_t partials = 0;
-    if (nph > 1) {
-        // at most kMfPhaseTiles iterations per workgroup keep their partial sums
-        grid = max(grid, (groups + kMfPhaseTiles - 1) / kMfPhaseTiles);
-        const int64_t nit_max = (groups + grid - 1) / grid;
-        partials = nit_max * TPW * kWave * 16;
+    const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (p.codes + kMfFixedLds)));
+    int64_t grid = max((int64_t)1, min(p.groups, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups));
+    grid = phase_grid(p, grid);
+    return launch_mf(a, (int)p.nph, (int)p.qph, grid, (size_t)(p.codes + partial_bytes(p, grid)), s);
+}
+
+hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxMulti) return hipErrorInvalidValue;
+    GroupArgs gs[kMaxMulti];
+    for (int i = 0; i < count; ++i) gs[i] = make_group_args(groups[i]);
+    const int64_t N = gs[0].N;
+    if (N <= 0) return hipSuccess;
+    Plan p[kMaxMulti];
+    int64_t bytes[kMaxMulti], total = 0, codes_max = 0;
+    for (int i = 0; i < count; ++i) {
+        p[i] = plan_group(gs[i]);
+        bytes[i] = group_tiles(gs[i]) * gs[i].K / 4;
+        total += bytes[i];
+        codes_max = max(codes_max, p[i].codes);
     }
-    return launch_mf(a, (int)nph, (int)qph, grid, (size_t)(codes + partials), s);
+    if (total == 0) return hipSuccess;
+    const int64_t tgroups = (N + 15) / 16;
+    // Workgroups per compute unit from the largest group's codes, then the
+    // grid split over the groups in proportion to their weight bytes (they
+    // run side by side and end together); one more pass if the partial sums
+    // of the phased groups leave room for fewer workgroups per unit.
+    int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (codes_max + kMfFixedLds)));
+    int64_t grid[kMaxMulti] = {};
+    int64_t shmem = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int64_t budget = max((int64_t)1, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups);
+        shmem = 0;
+        for (int i = 0; i < count; ++i) {
+            const int64_t share = (budget * bytes[i] + total / 2) / total;
+            grid[i] = phase_grid(p[i], max((int64_t)1, min(p[i].groups, share)));
+            shmem = max(shmem, p[i].codes + partial_bytes(p[i], grid[i]));
+        }
+        const int fit = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (shmem + kMfFixedLds)));
+        if (fit >= per_cu) break;
+        per_cu = fit;
+    }
+    MultiArgs m{};
+    int64_t start = 0;
+    for (int i = 0; i < kMaxMulti; ++i) {
+        const int j = i < count ? i : count - 1;
+        m.g[i] = gs[j];
+        m.nph[i] = (int)p[j].nph;
+        m.qph[i] = (int)p[j].qph;
+        m.start[i] = (int)start;
+        if (i < count) start += grid[i];
+    }
+    m.start[kMaxMulti] = (int)start;
+    auto kern = decode_mfma_multi_kernel<kMfWaves, kMfSplit, kMfRing>;
+    if (shmem > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)shmem);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)start, (unsigned)tgroups), dim3(kMfThreads),
+                       (size_t)shmem, s, m);
+    return hipGetLastError();
 }
 
 }  // namespace bt
