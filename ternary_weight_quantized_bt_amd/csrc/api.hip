@@ -407,9 +407,11 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         g.N = N;
         g.ydt = io->y_dtype;
     }
-    if (quantized && N > bt::kDot4MaxN && N < BT_PREFILL_MIN_N) {
-        // matrix-core decode: the four groups side by side in one launch
-        const hipError_t e = bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s);
+    if (quantized && N > bt::kDot4MaxN) {
+        // matrix-core decode or prefill: the four groups in one launch
+        const hipError_t e = N < BT_PREFILL_MIN_N
+                                 ? bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s)
+                                 : bt::launch_prefill_groups(groups, BT_LAYER_INPUTS, s);
         return e == hipSuccess ? ok() : hip_status(e, fn);
     }
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {

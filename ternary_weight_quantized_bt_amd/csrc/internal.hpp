@@ -69,6 +69,9 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s);
 hipError_t launch_decode_fused(const Group &g, const void *x, bt_dtype xdt, hipStream_t s);
 // Prefill path: tiled int8 matrix-core product.
 hipError_t launch_prefill(const Group &g, hipStream_t s);
+// Prefill of up to four groups, each with its own quantized input, in one
+// launch; results equal launch_prefill per group.
+hipError_t launch_prefill_groups(const Group *groups, int count, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cus();

@@ -29,6 +29,8 @@
 // of the token-major tile list -- each XCD then works through a contiguous
 // run of tiles that share activation rows, which stay in its L2.
 
+#include <algorithm>
+
 #include "group.hpp"
 
 namespace bt {
@@ -50,9 +52,11 @@ __device__ __forceinline__ v4i unpack_a(uint32_t word) {
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// One group's work; b is the workgroup's number among those of the group
+// (blockIdx.x of a launch for this group alone; a multiple of 8 apart from
+// the launch's own numbering, so the XCD of a workgroup is b % 8 either way).
 template <int RT, int TG, int WMW, int WNW, int S>
-__global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_kernel(GroupArgs a, int64_t mtiles) {
+__device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles, int64_t b) {
     constexpr int kWaves = WMW * WNW;
     constexpr int BN = 16 * TG * WNW;       // tokens per workgroup tile
     constexpr int BMT = RT * WMW;           // row tiles per workgroup tile
@@ -85,7 +89,7 @@ void prefill_kernel(GroupArgs a, int64_t mtiles) {
     const int64_t ntok = (N + BN - 1) / BN;
     const int64_t ntiles = mtiles * ntok;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    const int64_t idx = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int64_t idx = (b % kXcds) * per_xcd + b / kXcds;
     if (idx >= ntiles) return;  // whole workgroup
     const int64_t tn = idx / mtiles, tm = idx % mtiles;
     const int64_t tok0 = tn * BN;
@@ -215,6 +219,66 @@ void prefill_kernel(GroupArgs a, int64_t mtiles) {
 }
 
 template <int RT, int TG, int WMW, int WNW, int S>
+__global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(GroupArgs a, int64_t mtiles) {
+    prefill_group<RT, TG, WMW, WNW, S>(a, mtiles, blockIdx.x);
+}
+
+// Up to four groups (each with its own input) in one grid: workgroups
+// [start[i], start[i+1]) run group i; every range is a multiple of 8 long.
+constexpr int kMaxMulti = 4;
+struct MultiArgs {
+    GroupArgs g[kMaxMulti];
+    int64_t mtiles[kMaxMulti];
+    int start[kMaxMulti + 1];
+};
+
+template <int RT, int TG, int WMW, int WNW, int S>
+__global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_multi_kernel(MultiArgs m) {
+    const int b = (int)blockIdx.x;
+    if (b < m.start[1])
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[0], m.mtiles[0], b);
+    else if (b < m.start[2])
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[1], m.mtiles[1], b - m.start[1]);
+    else if (b < m.start[3])
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[2], m.mtiles[2], b - m.start[2]);
+    else
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[3], m.mtiles[3], b - m.start[3]);
+}
+
+// Workgroups of one group: its tiles, rounded up to a multiple of the XCDs.
+template <int RT, int TG, int WMW, int WNW>
+int64_t group_grid(const GroupArgs &a, int64_t &mtiles) {
+    constexpr int BMT = RT * WMW, BN = 16 * TG * WNW;
+    mtiles = (group_tiles(a) + BMT - 1) / BMT;
+    const int64_t ntiles = mtiles * ((a.N + BN - 1) / BN);
+    return (ntiles + kXcds - 1) / kXcds * kXcds;
+}
+
+template <int RT, int TG, int WMW, int WNW, int S>
+hipError_t launch_multi(const GroupArgs *gs, int count, hipStream_t s) {
+    // longest workgroups (largest K) first, so the short ones fill the tail
+    int order[kMaxMulti];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int x, int y) { return gs[x].K > gs[y].K; });
+    MultiArgs m{};
+    int64_t start = 0;
+    for (int i = 0; i < kMaxMulti; ++i) {
+        const int j = order[i < count ? i : count - 1];
+        m.g[i] = gs[j];
+        m.start[i] = (int)start;
+        const int64_t grid = group_grid<RT, TG, WMW, WNW>(gs[j], m.mtiles[i]);
+        if (i < count) start += grid;
+    }
+    m.start[kMaxMulti] = (int)start;
+    if (start == 0) return hipSuccess;
+    hipLaunchKernelGGL((prefill_multi_kernel<RT, TG, WMW, WNW, S>), dim3((unsigned)start),
+                       dim3(WMW * WNW * kWave), 0, s, m);
+    return hipGetLastError();
+}
+
+template <int RT, int TG, int WMW, int WNW, int S>
 hipError_t launch_tiles(const GroupArgs &a, hipStream_t s) {
     constexpr int BMT = RT * WMW, BN = 16 * TG * WNW;
     const int64_t mtiles = (group_tiles(a) + BMT - 1) / BMT;
@@ -227,12 +291,20 @@ hipError_t launch_tiles(const GroupArgs &a, hipStream_t s) {
 
 }  // namespace
 
+// 256 rows x 64 tokens per workgroup (4 waves of 64 x 64), 3 stages of
+// 16 KiB: two workgroups per CU.
 hipError_t launch_prefill(const Group &g, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const GroupArgs a = make_group_args(g);
-    // 256 rows x 64 tokens per workgroup (4 waves of 64 x 64), 3 stages of
-    // 16 KiB: two workgroups per CU.
     return launch_tiles<4, 4, 4, 1, 3>(a, s);
+}
+
+hipError_t launch_prefill_groups(const Group *groups, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxMulti) return hipErrorInvalidValue;
+    if (groups[0].N == 0) return hipSuccess;
+    GroupArgs gs[kMaxMulti];
+    for (int i = 0; i < count; ++i) gs[i] = make_group_args(groups[i]);
+    return launch_multi<4, 4, 4, 1, 3>(gs, count, s);
 }
 
 }  // namespace bt
