@@ -199,6 +199,61 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
         const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
         s_w[i] = packed_scale(tr.packed, tr.M, K);
     }
+
+    // bf16 output with all of the workgroup's row tiles in one projection
+    // (every tile but those at a projection boundary or past the end): the
+    // results of 16 tokens at a time go through LDS, token-major, and each
+    // token's BMT*16 consecutive outputs leave with 16-byte stores that
+    // cover whole rows (a lane's own 4 outputs per token would be 8-byte
+    // pieces 2*M bytes apart).  The B stages are free by then; sB0 and sB1
+    // alternate, so one barrier per token group orders the writes of one
+    // group and the reads of the previous one.
+    if constexpr (WNW == 1) {
+        const int64_t wt0 = tm * BMT;
+        bool whole = false;
+        TileRef tw{};
+        if (a.ydt == BT_BF16 && wt0 + BMT - 1 < total) {
+            tw = resolve_tile(a, wt0);
+            whole = resolve_tile(a, wt0 + BMT - 1).proj == tw.proj;
+        }
+        if (whole) {
+            constexpr int kRowsWg = BMT * kTileRows;     // outputs per token
+            constexpr int kPitch = 2 * kRowsWg + 16;     // LDS bytes per token (padded)
+            constexpr int kPerTok = 2 * kRowsWg / 16;    // 16-byte chunks per token
+            static_assert(16 * kPitch <= BN * kRow, "16 tokens fit one stage");
+            // row tiles of one projection share its scale
+            const float sw = s_w[0];
+            __syncthreads();  // every wave is done with the B stages (and their loads)
+#pragma unroll
+            for (int g = 0; g < TG; ++g) {
+                int8_t *T = (g & 1) ? sB1 : sB0;
+                const int64_t tc = min(tok0 + g * 16 + r, N - 1);
+                const float f = token_factor(sw, a.xs[tc]);
+                const int32_t sub = a.xsum[tc];
+#pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    const v4i v = acc[i][g];
+                    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<v2u *>(T + r * kPitch + 2 * ((wm * RT + i) * kTileRows + 4 * h)) =
+                        v2u{f32x2_to_bf16x2(__fmul_rn((float)(v.x - sub), f),
+                                            __fmul_rn((float)(v.y - sub), f)),
+                            f32x2_to_bf16x2(__fmul_rn((float)(v.z - sub), f),
+                                            __fmul_rn((float)(v.w - sub), f))};
+                }
+                __syncthreads();
+                for (int c = (int)threadIdx.x; c < 16 * kPerTok; c += kWaves * kWave) {
+                    const int tl = c / kPerTok, col = c % kPerTok;
+                    const int64_t tok = tok0 + g * 16 + tl;
+                    if (tok < N)
+                        *to_global(reinterpret_cast<v4u *>(reinterpret_cast<uint16_t *>(tw.y) + tok * tw.M +
+                                                           tw.mt * kTileRows) + col) =
+                            *reinterpret_cast<const v4u *>(T + tl * kPitch + 16 * col);
+                }
+            }
+            return;
+        }
+    }
+
 #pragma unroll
     for (int g = 0; g < TG; ++g) {
         const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;

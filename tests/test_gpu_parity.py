@@ -192,14 +192,26 @@ def test_batched_decode_three_k_phases_sampled():
     assert_equal(y[:, rows], acc, "three phases")
 
 
-def test_gemv_and_gemm_agree_bitwise():
-    M, K = 208, 2304
-    for N in (1, 4, 5, 64, 257):
+@pytest.mark.parametrize("M,K,Ns", [
+    (208, 2304, (1, 4, 5, 64, 257)),
+    # 35 row tiles: two workgroup tiles of 256 whole rows (bf16 results leave
+    # through LDS) and a partial one (direct stores); ragged token tiles
+    (560, 1024, (128, 130, 200, 257)),
+])
+def test_gemv_and_gemm_agree_bitwise(M, K, Ns):
+    for N in Ns:
         _, _, packed, xq, xs, xsum = _case(M, K, N, 99 + N)
         for ydt in (bt.BT_F32, bt.BT_BF16, bt.BT_I32):
             a = bt.gemv(packed, M, K, xq, xs, xsum, ydt)
             b = bt.gemm(packed, M, K, xq, xs, xsum, ydt)
             assert torch.equal(a, b), (N, ydt)
+
+
+def test_prefill_bf16_whole_tiles_against_oracle():
+    M, K, N = 560, 1024, 200
+    ref_packed, ref, packed, xq, xs, xsum = _case(M, K, N, 4242)
+    y = bt.gemm(packed, M, K, xq, xs, xsum, bt.BT_BF16)
+    assert_rel_close(as_f64(y), ref["y"], RTOL[bt.BT_BF16], "prefill bf16")
 
 
 def test_special_weights_and_zero_tokens():
