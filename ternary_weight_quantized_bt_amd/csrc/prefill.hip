@@ -163,6 +163,9 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
             v4i bcur[TG], bnext[TG];
 #pragma unroll
             for (int g = 0; g < TG; ++g) bcur[g] = read_b(s, 0, g);
+            v4i A[RT];
+#pragma unroll
+            for (int i = 0; i < RT; ++i) A[i] = unpack_a(ar[s][i][0]);
             // The next step's fragments are read while this step's matrix
             // instructions run; a scheduling fence per step keeps the
             // scheduler from hoisting every step's operands at once.
@@ -173,9 +176,13 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
 #pragma unroll
                     for (int g = 0; g < TG; ++g) bnext[g] = read_b(s, t + 1, g);
                 }
-                v4i A[RT];
+                // next step's A operands, unpacked between this step's
+                // matrix instructions (one instruction, two VALU ops)
+                v4i An[RT];
+                if (t < 3) {
 #pragma unroll
-                for (int i = 0; i < RT; ++i) A[i] = unpack_a(ar[s][i][t]);
+                    for (int i = 0; i < RT; ++i) An[i] = unpack_a(ar[s][i][t + 1]);
+                }
 #pragma unroll
                 for (int g = 0; g < TG; ++g)
 #pragma unroll
@@ -185,6 +192,13 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
                 if (t < 3) {
 #pragma unroll
                     for (int g = 0; g < TG; ++g) bcur[g] = bnext[g];
+#pragma unroll
+                    for (int i = 0; i < RT; ++i) A[i] = An[i];
+                }
+#pragma unroll
+                for (int k = 0; k < RT * TG; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
                 }
             }
         }
@@ -346,12 +360,14 @@ hipError_t launch_tiles(const GroupArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// 256 rows x 64 tokens per workgroup (4 waves of 64 x 64), 3 stages of
-// 16 KiB: two workgroups per CU.
+// 256 rows x 64 tokens per workgroup (4 waves of 64 x 64), two stages of
+// 16 KiB (the next block in flight while one is consumed; a third stage
+// measured slower -- it costs 16 more registers per lane): two workgroups
+// per CU.
 hipError_t launch_prefill(const Group &g, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const GroupArgs a = make_group_args(g);
-    return launch_tiles<4, 4, 4, 1, 3>(a, s);
+    return launch_tiles<4, 4, 4, 1, 2>(a, s);
 }
 
 hipError_t launch_prefill_groups(const Group *groups, int count, hipStream_t s) {
@@ -359,7 +375,7 @@ hipError_t launch_prefill_groups(const Group *groups, int count, hipStream_t s) 
     if (groups[0].N == 0) return hipSuccess;
     GroupArgs gs[kMaxMulti];
     for (int i = 0; i < count; ++i) gs[i] = make_group_args(groups[i]);
-    return launch_multi<4, 4, 4, 1, 3>(gs, count, s);
+    return launch_multi<4, 4, 4, 1, 2>(gs, count, s);
 }
 
 }  // namespace bt

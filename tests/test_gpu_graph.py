@@ -54,3 +54,40 @@ def test_graph_replays_match_eager(N):
                 assert torch.equal(y, e), f"replay {rep} differs"
         step()                       # eager launch between replays
         torch.cuda.synchronize()
+
+
+def test_weight_quantizer_graph_replays():
+    # the state block is cleared by a fill kernel, so replays start clean
+    M, K = 64, 1024
+    ws_bytes = bt.bt_quantize_weights_workspace_bytes()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    w = W.float_weights(M, K, "wide", 3).to(DEV)
+    packed = torch.empty(bt.bt_packed_bytes(M, K), dtype=torch.uint8, device=DEV)
+    stats = torch.empty(2, dtype=torch.float32, device=DEV)
+
+    def step():
+        bt.bt_quantize_weights(w, bt.BT_F32, M, K, bt.BT_WSCALE_ABSMEAN, 1e-5, packed,
+                               stats, ws, ws_bytes)
+
+    step()
+    torch.cuda.synchronize()
+    ref_packed, ref_stats = packed.clone(), stats.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        packed.fill_(0)
+        stats.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(packed, ref_packed), f"replay {rep} packed"
+        assert torch.equal(stats, ref_stats), f"replay {rep} stats"
+        step()
+        torch.cuda.synchronize()
