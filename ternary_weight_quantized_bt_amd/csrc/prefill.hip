@@ -52,11 +52,13 @@ __device__ __forceinline__ v4i unpack_a(uint32_t word) {
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// One group's work; b is the workgroup's number among those of the group
-// (blockIdx.x of a launch for this group alone; a multiple of 8 apart from
-// the launch's own numbering, so the XCD of a workgroup is b % 8 either way).
+// One group's work; b is the workgroup's number among the G that run the
+// group (blockIdx.x and gridDim.x of a launch for this group alone; b is a
+// multiple of 8 apart from the launch's own numbering, so the XCD of a
+// workgroup is b % 8 either way).
 template <int RT, int TG, int WMW, int WNW, int S>
-__device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles, int64_t b) {
+__device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles, int64_t b,
+                                              int64_t G) {
     constexpr int kWaves = WMW * WNW;
     constexpr int BN = 16 * TG * WNW;       // tokens per workgroup tile
     constexpr int BMT = RT * WMW;           // row tiles per workgroup tile
@@ -89,208 +91,223 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
     const int64_t ntok = (N + BN - 1) / BN;
     const int64_t ntiles = mtiles * ntok;
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-    const int64_t idx = (b % kXcds) * per_xcd + b / kXcds;
-    if (idx >= ntiles) return;  // whole workgroup
-    const int64_t tn = idx / mtiles, tm = idx % mtiles;
-    const int64_t tok0 = tn * BN;
+    // The workgroup takes list positions b, b + G, b + 2G, ... (G is a
+    // multiple of 8, so they all belong to its own XCD's run).  A launch for
+    // one group caps G at the resident workgroups, so the grid is persistent
+    // and one tile's stores drain while the next computes; the four-group
+    // launch gives every position its own workgroup.
+    for (int64_t j = b;; j += G) {
+        const int64_t idx = (j % kXcds) * per_xcd + j / kXcds;
+        if (j / kXcds >= per_xcd || idx >= ntiles) break;  // whole workgroup
+        const int64_t tn = idx / mtiles, tm = idx % mtiles;
+        const int64_t tok0 = tn * BN;
 
-    // This wave's row tiles (clamped to the last tile past the end; their
-    // results are not stored): wave-uniform base addresses plus the lane's
-    // 16-byte offset at each load.
-    const uint8_t *abase[RT];
+        // This wave's row tiles (clamped to the last tile past the end; their
+        // results are not stored): wave-uniform base addresses plus the lane's
+        // 16-byte offset at each load.
+        const uint8_t *abase[RT];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-        const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
-        abase[i] = tr.packed + tr.mt * qb * kTileBytes;
-    }
+        for (int i = 0; i < RT; ++i) {
+            const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
+            abase[i] = tr.packed + tr.mt * qb * kTileBytes;
+        }
 
-    // All loads of block q (clamped to the last block, so every call issues
-    // exactly kVm operations and the wait counts below stay exact): the A
-    // slots into registers, the token block into LDS stage st.  Each 1 KiB
-    // direct load covers 4 tokens; lane l fills position l%16 of token l/16
-    // with global chunk (l%16) ^ (token % 16).
-    v4u ar[S][RT];
-    auto issue = [&](int64_t q, int st) {
-        q = min(q, qb - 1);
+        // All loads of block q (clamped to the last block, so every call issues
+        // exactly kVm operations and the wait counts below stay exact): the A
+        // slots into registers, the token block into LDS stage st.  Each 1 KiB
+        // direct load covers 4 tokens; lane l fills position l%16 of token l/16
+        // with global chunk (l%16) ^ (token % 16).
+        v4u ar[S][RT];
+        auto issue = [&](int64_t q, int st) {
+            q = min(q, qb - 1);
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+                ar[st][i] = *to_global(reinterpret_cast<const v4u *>(abase[i] + q * kTileBytes) + lane);
+#pragma unroll
+            for (int i = 0; i < kDmaW; ++i) {
+                const int d = wave * kDmaW + i;   // 1 KiB unit of the block
+                const int tl = d * 4 + lane / 16;  // token within the tile
+                const int64_t tok = min(tok0 + tl, N - 1);
+                const int c = (lane % 16) ^ (tl % 16);
+                const int8_t *src = a.xq + tok * K + q * kTileCols + 16 * c;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)src,
+                    (__attribute__((address_space(3))) void *)(stage(st) + d * 1024), 16, 0, 0);
+            }
+        };
+        // B fragment of token group g, 64-column step t, from stage st: token
+        // g*16 + r of this wave, chunk 4t + h, stored at (4t + h) ^ (token % 16).
+        auto read_b = [&](int st, int t, int g) {
+            return *reinterpret_cast<const v4i *>(stage(st) + (wn * 16 * TG + g * 16 + r) * kRow +
+                                                  16 * ((4 * t + h) ^ r));
+        };
+
+        v4i acc[RT][TG];
 #pragma unroll
         for (int i = 0; i < RT; ++i)
-            ar[st][i] = *to_global(reinterpret_cast<const v4u *>(abase[i] + q * kTileBytes) + lane);
 #pragma unroll
-        for (int i = 0; i < kDmaW; ++i) {
-            const int d = wave * kDmaW + i;   // 1 KiB unit of the block
-            const int tl = d * 4 + lane / 16;  // token within the tile
-            const int64_t tok = min(tok0 + tl, N - 1);
-            const int c = (lane % 16) ^ (tl % 16);
-            const int8_t *src = a.xq + tok * K + q * kTileCols + 16 * c;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)src,
-                (__attribute__((address_space(3))) void *)(stage(st) + d * 1024), 16, 0, 0);
-        }
-    };
-    // B fragment of token group g, 64-column step t, from stage st: token
-    // g*16 + r of this wave, chunk 4t + h, stored at (4t + h) ^ (token % 16).
-    auto read_b = [&](int st, int t, int g) {
-        return *reinterpret_cast<const v4i *>(stage(st) + (wn * 16 * TG + g * 16 + r) * kRow +
-                                              16 * ((4 * t + h) ^ r));
-    };
+            for (int g = 0; g < TG; ++g) acc[i][g] = v4i{0, 0, 0, 0};
 
-    v4i acc[RT][TG];
+        // Prologue: blocks 0 .. S-2 in flight.
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int g = 0; g < TG; ++g) acc[i][g] = v4i{0, 0, 0, 0};
+        for (int s = 0; s < S - 1; ++s) issue(s, s);
 
-    // Prologue: blocks 0 .. S-2 in flight.
+        // Block q: wait until it has landed for every wave (S-2 younger blocks
+        // may stay in flight), barrier -- which also means every wave is done
+        // with block q-1 -- then refill that block's stage with block q+S-1 and
+        // compute block q.  Unrolled by S so stages and registers are static.
+        for (int64_t q0 = 0; q0 < qb; q0 += S) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) issue(s, s);
-
-    // Block q: wait until it has landed for every wave (S-2 younger blocks
-    // may stay in flight), barrier -- which also means every wave is done
-    // with block q-1 -- then refill that block's stage with block q+S-1 and
-    // compute block q.  Unrolled by S so stages and registers are static.
-    for (int64_t q0 = 0; q0 < qb; q0 += S) {
+            for (int s = 0; s < S; ++s) {
+                const int64_t q = q0 + s;
+                if (q >= qb) break;  // uniform
+                // Block q's direct loads are complete for this wave once at most
+                // the S-2 younger blocks are outstanding; the bare barrier (no
+                // fence: a fence would drain those younger loads too) then makes
+                // every wave's part of the block visible.
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * kVm));
+                __builtin_amdgcn_s_barrier();
+                // (two stages: the wait above is for zero operations, so the
+                // clamped reload past the last block can be left out)
+                if (S > 2 || q + 1 < qb) issue(q + S - 1, (s + S - 1) % S);
+                v4i bcur[TG], bnext[TG];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int64_t q = q0 + s;
-            if (q >= qb) break;  // uniform
-            // Block q's direct loads are complete for this wave once at most
-            // the S-2 younger blocks are outstanding; the bare barrier (no
-            // fence: a fence would drain those younger loads too) then makes
-            // every wave's part of the block visible.
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * kVm));
-            __builtin_amdgcn_s_barrier();
-            issue(q + S - 1, (s + S - 1) % S);
-            v4i bcur[TG], bnext[TG];
+                for (int g = 0; g < TG; ++g) bcur[g] = read_b(s, 0, g);
+                v4i A[RT];
 #pragma unroll
-            for (int g = 0; g < TG; ++g) bcur[g] = read_b(s, 0, g);
-            v4i A[RT];
+                for (int i = 0; i < RT; ++i) A[i] = unpack_a(ar[s][i][0]);
+                // The next step's fragments are read while this step's matrix
+                // instructions run; a scheduling fence per step keeps the
+                // scheduler from hoisting every step's operands at once.
 #pragma unroll
-            for (int i = 0; i < RT; ++i) A[i] = unpack_a(ar[s][i][0]);
-            // The next step's fragments are read while this step's matrix
-            // instructions run; a scheduling fence per step keeps the
-            // scheduler from hoisting every step's operands at once.
+                for (int t = 0; t < 4; ++t) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t < 3) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (t < 3) {
+                        for (int g = 0; g < TG; ++g) bnext[g] = read_b(s, t + 1, g);
+                    }
+                    // next step's A operands, unpacked between this step's
+                    // matrix instructions (one instruction, two VALU ops)
+                    v4i An[RT];
+                    if (t < 3) {
 #pragma unroll
-                    for (int g = 0; g < TG; ++g) bnext[g] = read_b(s, t + 1, g);
-                }
-                // next step's A operands, unpacked between this step's
-                // matrix instructions (one instruction, two VALU ops)
-                v4i An[RT];
-                if (t < 3) {
+                        for (int i = 0; i < RT; ++i) An[i] = unpack_a(ar[s][i][t + 1]);
+                    }
 #pragma unroll
-                    for (int i = 0; i < RT; ++i) An[i] = unpack_a(ar[s][i][t + 1]);
-                }
+                    for (int g = 0; g < TG; ++g)
 #pragma unroll
-                for (int g = 0; g < TG; ++g)
+                        for (int i = 0; i < RT; ++i)
+                            acc[i][g] =
+                                __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], bcur[g], acc[i][g], 0, 0, 0);
+                    if (t < 3) {
 #pragma unroll
-                    for (int i = 0; i < RT; ++i)
-                        acc[i][g] =
-                            __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], bcur[g], acc[i][g], 0, 0, 0);
-                if (t < 3) {
+                        for (int g = 0; g < TG; ++g) bcur[g] = bnext[g];
 #pragma unroll
-                    for (int g = 0; g < TG; ++g) bcur[g] = bnext[g];
+                        for (int i = 0; i < RT; ++i) A[i] = An[i];
+                    }
 #pragma unroll
-                    for (int i = 0; i < RT; ++i) A[i] = An[i];
-                }
-#pragma unroll
-                for (int k = 0; k < RT * TG; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+                    for (int k = 0; k < RT * TG; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+                    }
                 }
             }
         }
-    }
 
-    // Epilogue: lane (r, h) holds rows 4h..4h+3 of each row tile for token
-    // g*16 + r of each group.  Per-row-tile values are wave-uniform; token
-    // values are loaded from a clamped index so only the stores branch.
-    float s_w[RT];
+        // Epilogue: lane (r, h) holds rows 4h..4h+3 of each row tile for token
+        // g*16 + r of each group.  Per-row-tile values are wave-uniform; token
+        // values are loaded from a clamped index so only the stores branch.
+        float s_w[RT];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-        const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
-        s_w[i] = packed_scale(tr.packed, tr.M, K);
-    }
-
-    // bf16 output with all of the workgroup's row tiles in one projection
-    // (every tile but those at a projection boundary or past the end): the
-    // results of 16 tokens at a time go through LDS, token-major, and each
-    // token's BMT*16 consecutive outputs leave with 16-byte stores that
-    // cover whole rows (a lane's own 4 outputs per token would be 8-byte
-    // pieces 2*M bytes apart).  The B stages are free by then; sB0 and sB1
-    // alternate, so one barrier per token group orders the writes of one
-    // group and the reads of the previous one.
-    if constexpr (WNW == 1) {
-        const int64_t wt0 = tm * BMT;
-        bool whole = false;
-        TileRef tw{};
-        if (a.ydt == BT_BF16 && wt0 + BMT - 1 < total) {
-            tw = resolve_tile(a, wt0);
-            whole = resolve_tile(a, wt0 + BMT - 1).proj == tw.proj;
+        for (int i = 0; i < RT; ++i) {
+            const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
+            s_w[i] = packed_scale(tr.packed, tr.M, K);
         }
-        if (whole) {
-            constexpr int kRowsWg = BMT * kTileRows;     // outputs per token
-            constexpr int kPitch = 2 * kRowsWg + 16;     // LDS bytes per token (padded)
-            constexpr int kPerTok = 2 * kRowsWg / 16;    // 16-byte chunks per token
-            static_assert(16 * kPitch <= BN * kRow, "16 tokens fit one stage");
-            // row tiles of one projection share its scale
-            const float sw = s_w[0];
-            __syncthreads();  // every wave is done with the B stages (and their loads)
+
+        // bf16 output with all of the workgroup's row tiles in one projection
+        // (every tile but those at a projection boundary or past the end): the
+        // results of 16 tokens at a time go through LDS, token-major, and each
+        // token's BMT*16 consecutive outputs leave with 16-byte stores that
+        // cover whole rows (a lane's own 4 outputs per token would be 8-byte
+        // pieces 2*M bytes apart).  The B stages are free by then; sB0 and sB1
+        // alternate, so one barrier per token group orders the writes of one
+        // group and the reads of the previous one.
+        bool stored = false;
+        if constexpr (WNW == 1) {
+            const int64_t wt0 = tm * BMT;
+            bool whole = false;
+            TileRef tw{};
+            if (a.ydt == BT_BF16 && wt0 + BMT - 1 < total) {
+                tw = resolve_tile(a, wt0);
+                whole = resolve_tile(a, wt0 + BMT - 1).proj == tw.proj;
+            }
+            if (whole) {
+                constexpr int kRowsWg = BMT * kTileRows;     // outputs per token
+                constexpr int kPitch = 2 * kRowsWg + 16;     // LDS bytes per token (padded)
+                constexpr int kPerTok = 2 * kRowsWg / 16;    // 16-byte chunks per token
+                static_assert(16 * kPitch <= BN * kRow, "16 tokens fit one stage");
+                // row tiles of one projection share its scale
+                const float sw = s_w[0];
+                __syncthreads();  // every wave is done with the B stages (and their loads)
+#pragma unroll
+                for (int g = 0; g < TG; ++g) {
+                    int8_t *T = (g & 1) ? sB1 : sB0;
+                    const int64_t tc = min(tok0 + g * 16 + r, N - 1);
+                    const float f = token_factor(sw, a.xs[tc]);
+                    const int32_t sub = a.xsum[tc];
+#pragma unroll
+                    for (int i = 0; i < RT; ++i) {
+                        const v4i v = acc[i][g];
+                        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<v2u *>(T + r * kPitch + 2 * ((wm * RT + i) * kTileRows + 4 * h)) =
+                            v2u{f32x2_to_bf16x2(__fmul_rn((float)(v.x - sub), f),
+                                                __fmul_rn((float)(v.y - sub), f)),
+                                f32x2_to_bf16x2(__fmul_rn((float)(v.z - sub), f),
+                                                __fmul_rn((float)(v.w - sub), f))};
+                    }
+                    __syncthreads();
+                    for (int c = (int)threadIdx.x; c < 16 * kPerTok; c += kWaves * kWave) {
+                        const int tl = c / kPerTok, col = c % kPerTok;
+                        const int64_t tok = tok0 + g * 16 + tl;
+                        if (tok < N)
+                            *to_global(reinterpret_cast<v4u *>(reinterpret_cast<uint16_t *>(tw.y) + tok * tw.M +
+                                                               tw.mt * kTileRows) + col) =
+                                *reinterpret_cast<const v4u *>(T + tl * kPitch + 16 * col);
+                    }
+                }
+                stored = true;
+            }
+        }
+
+        if (!stored) {
 #pragma unroll
             for (int g = 0; g < TG; ++g) {
-                int8_t *T = (g & 1) ? sB1 : sB0;
-                const int64_t tc = min(tok0 + g * 16 + r, N - 1);
-                const float f = token_factor(sw, a.xs[tc]);
+                const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;
+                const int64_t tc = min(tok, N - 1);
+                const float s_a = a.xs[tc];
                 const int32_t sub = a.xsum[tc];
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
-                    const v4i v = acc[i][g];
-                    typedef unsigned v2u __attribute__((ext_vector_type(2)));
-                    *reinterpret_cast<v2u *>(T + r * kPitch + 2 * ((wm * RT + i) * kTileRows + 4 * h)) =
-                        v2u{f32x2_to_bf16x2(__fmul_rn((float)(v.x - sub), f),
-                                            __fmul_rn((float)(v.y - sub), f)),
-                            f32x2_to_bf16x2(__fmul_rn((float)(v.z - sub), f),
-                                            __fmul_rn((float)(v.w - sub), f))};
+                    const int64_t t = tm * BMT + wm * RT + i;
+                    if (t >= total) continue;  // uniform
+                    const TileRef tr = resolve_tile(a, t);
+                    const float f = token_factor(s_w[i], s_a);
+                    const int64_t base = tok * tr.M + tr.mt * kTileRows + 4 * h;
+                    if (tok < N) store_out4(tr.y, a.ydt, base, acc[i][g], sub, f);
                 }
-                __syncthreads();
-                for (int c = (int)threadIdx.x; c < 16 * kPerTok; c += kWaves * kWave) {
-                    const int tl = c / kPerTok, col = c % kPerTok;
-                    const int64_t tok = tok0 + g * 16 + tl;
-                    if (tok < N)
-                        *to_global(reinterpret_cast<v4u *>(reinterpret_cast<uint16_t *>(tw.y) + tok * tw.M +
-                                                           tw.mt * kTileRows) + col) =
-                            *reinterpret_cast<const v4u *>(T + tl * kPitch + 16 * col);
-                }
+                __builtin_amdgcn_sched_barrier(0);  // keep one token group's values live at a time
             }
-            return;
         }
-    }
-
-#pragma unroll
-    for (int g = 0; g < TG; ++g) {
-        const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;
-        const int64_t tc = min(tok, N - 1);
-        const float s_a = a.xs[tc];
-        const int32_t sub = a.xsum[tc];
-#pragma unroll
-        for (int i = 0; i < RT; ++i) {
-            const int64_t t = tm * BMT + wm * RT + i;
-            if (t >= total) continue;  // uniform
-            const TileRef tr = resolve_tile(a, t);
-            const float f = token_factor(s_w[i], s_a);
-            const int64_t base = tok * tr.M + tr.mt * kTileRows + 4 * h;
-            if (tok < N) store_out4(tr.y, a.ydt, base, acc[i][g], sub, f);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep one token group's values live at a time
+        // every wave is done with the stages (and their loads) before the next
+        // tile's first loads go into them
+        __syncthreads();
     }
 }
 
 template <int RT, int TG, int WMW, int WNW, int S>
 __global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(GroupArgs a, int64_t mtiles) {
-    prefill_group<RT, TG, WMW, WNW, S>(a, mtiles, blockIdx.x);
+    prefill_group<RT, TG, WMW, WNW, S>(a, mtiles, blockIdx.x, gridDim.x);
 }
 
 // Up to four groups (each with its own input) in one grid: workgroups
@@ -307,13 +324,13 @@ __global__ __launch_bounds__(WMW * WNW * kWave) __attribute__((amdgpu_waves_per_
 void prefill_multi_kernel(MultiArgs m) {
     const int b = (int)blockIdx.x;
     if (b < m.start[1])
-        prefill_group<RT, TG, WMW, WNW, S>(m.g[0], m.mtiles[0], b);
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[0], m.mtiles[0], b, m.start[1]);
     else if (b < m.start[2])
-        prefill_group<RT, TG, WMW, WNW, S>(m.g[1], m.mtiles[1], b - m.start[1]);
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[1], m.mtiles[1], b - m.start[1], m.start[2] - m.start[1]);
     else if (b < m.start[3])
-        prefill_group<RT, TG, WMW, WNW, S>(m.g[2], m.mtiles[2], b - m.start[2]);
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[2], m.mtiles[2], b - m.start[2], m.start[3] - m.start[2]);
     else
-        prefill_group<RT, TG, WMW, WNW, S>(m.g[3], m.mtiles[3], b - m.start[3]);
+        prefill_group<RT, TG, WMW, WNW, S>(m.g[3], m.mtiles[3], b - m.start[3], m.start[4] - m.start[3]);
 }
 
 // Workgroups of one group: its tiles, rounded up to a multiple of the XCDs.
@@ -325,9 +342,16 @@ int64_t group_grid(const GroupArgs &a, int64_t &mtiles) {
     return (ntiles + kXcds - 1) / kXcds * kXcds;
 }
 
+// Resident workgroups of a persistent grid: two per CU (registers), a
+// multiple of the XCD count.
+inline int64_t prefill_slots() { return max((int64_t)kXcds, (int64_t)device_cus() * 2 / kXcds * kXcds); }
+
 template <int RT, int TG, int WMW, int WNW, int S>
 hipError_t launch_multi(const GroupArgs *gs, int count, hipStream_t s) {
-    // longest workgroups (largest K) first, so the short ones fill the tail
+    // One workgroup per tile here (not persistent): the hardware hands the
+    // next workgroup to whichever slot frees up, which balances the groups'
+    // different tile costs better than any static split of the slots
+    // (measured).  Largest K first, so the cheap tiles fill the tail.
     int order[kMaxMulti];
     for (int i = 0; i < count; ++i) order[i] = i;
     std::stable_sort(order, order + count, [&](int x, int y) { return gs[x].K > gs[y].K; });
@@ -349,10 +373,8 @@ hipError_t launch_multi(const GroupArgs *gs, int count, hipStream_t s) {
 
 template <int RT, int TG, int WMW, int WNW, int S>
 hipError_t launch_tiles(const GroupArgs &a, hipStream_t s) {
-    constexpr int BMT = RT * WMW, BN = 16 * TG * WNW;
-    const int64_t mtiles = (group_tiles(a) + BMT - 1) / BMT;
-    const int64_t ntiles = mtiles * ((a.N + BN - 1) / BN);
-    const int64_t grid = (ntiles + kXcds - 1) / kXcds * kXcds;
+    int64_t mtiles;
+    const int64_t grid = min(group_grid<RT, TG, WMW, WNW>(a, mtiles), prefill_slots());
     hipLaunchKernelGGL((prefill_kernel<RT, TG, WMW, WNW, S>), dim3((unsigned)grid),
                        dim3(WMW * WNW * kWave), 0, s, a, mtiles);
     return hipGetLastError();

@@ -207,6 +207,18 @@ def test_gemv_and_gemm_agree_bitwise(M, K, Ns):
             assert torch.equal(a, b), (N, ydt)
 
 
+def test_prefill_persistent_workgroups_take_several_tiles():
+    # 16 x 33 = 528 workgroup tiles, more than the resident workgroups, so
+    # the persistent grid gives some of them two tiles (and a ragged last
+    # token tile); every output against the oracle's int32 sums, bf16 too
+    M, K, N = 4096, 512, 2049
+    ref_packed, ref, packed, xq, xs, xsum = _case(M, K, N, 777)
+    y = bt.gemm(packed, M, K, xq, xs, xsum, bt.BT_I32)
+    assert_equal(to_np(y), ref["acc"], "persistent prefill")
+    yb = bt.gemm(packed, M, K, xq, xs, xsum, bt.BT_BF16)
+    assert_rel_close(as_f64(yb), ref["y"], RTOL[bt.BT_BF16], "persistent prefill bf16")
+
+
 def test_prefill_bf16_whole_tiles_against_oracle():
     M, K, N = 560, 1024, 200
     ref_packed, ref, packed, xq, xs, xsum = _case(M, K, N, 4242)
