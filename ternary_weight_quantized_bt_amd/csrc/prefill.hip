@@ -363,6 +363,7 @@ hipError_t launch_multi(const GroupArgs *gs, int count, hipStream_t s) {
         m.start[i] = (int)start;
         const int64_t grid = group_grid<RT, TG, WMW, WNW>(gs[j], m.mtiles[i]);
         if (i < count) start += grid;
+        if (start > INT32_MAX) return hipErrorInvalidConfiguration;  // grid.x limit
     }
     m.start[kMaxMulti] = (int)start;
     if (start == 0) return hipSuccess;

@@ -94,3 +94,27 @@ def test_without_stats_output():
                            packed, None, ws, ws.numel())
     ref, _, _ = wq.quantize_weights(w.numpy(), "absmean", 0.0)
     assert_equal(to_np(packed), ref, "packed bytes")
+
+
+def test_full_size_gate_matrix_sampled_rows():
+    # the 28672 x 8192 bf16 gate/up matrix of the 70B-class block, in the
+    # configuration the benchmark times: the statistic and the divisor over
+    # the whole tensor bit for bit, and 64 sampled rows of codes against the
+    # oracle's RoundClip with that divisor
+    M, K = 28672, 8192
+    print("weight quantizer: full-size gate matrix", flush=True)
+    w = W.float_weights(M, K, "normal", 77, "bf16", device=DEV)
+    packed, stats = bt.quantize_weights(w, "absmean", 1e-5)
+    bits = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    s = wq.abs_mean(bits)
+    d = np.float32(s + np.float32(1e-5))
+    st = to_np(stats)
+    assert st[0].view(np.uint32) == np.float32(s).view(np.uint32), (st[0], s)
+    assert st[1].view(np.uint32) == d.view(np.uint32), (st[1], d)
+    rows = np.sort(np.random.default_rng(5).choice(M, 64, replace=False))
+    got = to_np(bt.unpack(packed, M, K))[rows]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        want = wq.round_clip(wq.as_f32(bits[rows]) / d)
+    assert_equal(got, want, "sampled rows of codes")
+    tail = to_np(packed[M * K // 4: M * K // 4 + 4])
+    assert tail.view(np.float32)[0] == d  # the stored scale is the divisor
