@@ -43,11 +43,12 @@ namespace bt {
 
 namespace {
 
-// Launch shape: 8 waves per workgroup, K split over all 8, 4 slot loads in
-// flight per wave.
+// Launch shape: 8 waves per workgroup, K split over 4 of them (two tiles per
+// iteration: 3 % faster than one tile split over all 8 at 8 tokens), 4 slot
+// loads in flight per wave.
 constexpr int kMfWaves = 8;
 constexpr int kMfThreads = kMfWaves * kWave;
-constexpr int kMfSplit = 8;
+constexpr int kMfSplit = 4;
 constexpr int kMfRing = 4;
 // LDS of one compute unit and the part a workgroup may use for token codes.
 constexpr int64_t kLdsPerCu = 160 * 1024;

@@ -269,10 +269,11 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
                     for (int c = (int)threadIdx.x; c < 16 * kPerTok; c += kWaves * kWave) {
                         const int tl = c / kPerTok, col = c % kPerTok;
                         const int64_t tok = tok0 + g * 16 + tl;
-                        if (tok < N)
-                            *to_global(reinterpret_cast<v4u *>(reinterpret_cast<uint16_t *>(tw.y) + tok * tw.M +
-                                                               tw.mt * kTileRows) + col) =
-                                *reinterpret_cast<const v4u *>(T + tl * kPitch + 16 * col);
+                        if (tok < N)  // written once: non-temporal
+                            __builtin_nontemporal_store(
+                                *reinterpret_cast<const v4u *>(T + tl * kPitch + 16 * col),
+                                to_global(reinterpret_cast<v4u *>(reinterpret_cast<uint16_t *>(tw.y) +
+                                                                  tok * tw.M + tw.mt * kTileRows) + col));
                     }
                 }
                 stored = true;
