@@ -180,11 +180,18 @@ def time_region(fn, reps):
     return start.elapsed_time(end) / 1e3, wall
 
 
-def run_steps(model, steps, warmup, use_graph, step=None):
-    """Returns (seconds per step, wall seconds of the timed region)."""
+def run_steps(model, steps, warmup, use_graph, step=None, per_graph=1):
+    """Returns (seconds per step, wall seconds of the timed region).
+
+    With a graph, `per_graph` consecutive steps are captured in one graph and
+    the graph is replayed steps / per_graph times (every step still runs in
+    full; only the host's per-replay launch cost is shared, as when a graph
+    holds a whole model's blocks)."""
     import torch
     step = step or model.step
     if use_graph:
+        if steps % per_graph or warmup % per_graph:
+            raise ValueError("steps and warmup must be multiples of per_graph")
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -193,13 +200,14 @@ def run_steps(model, steps, warmup, use_graph, step=None):
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step()
+            for _ in range(per_graph):
+                step()
         fn = g.replay
     else:
-        fn = step
-    for _ in range(warmup):
+        fn, per_graph = step, 1
+    for _ in range(warmup // per_graph):
         fn()
-    t, wall = time_region(fn, steps)
+    t, wall = time_region(fn, steps // per_graph)
     return t / steps, wall
 
 
@@ -330,7 +338,9 @@ def prefill_extra(steps, warmup, use_graph):
     wl = W.PREFILL2B_N2048
     m = Model(wl, 1, "cuda:0")
     m.set_tokens(2048)
-    sec, _ = run_steps(m, steps, warmup, use_graph)
+    # one block per step: all timed steps in one graph (a model's graph holds
+    # its 30 blocks), so one replay launch is not charged to every block
+    sec, _ = run_steps(m, steps, steps, use_graph, per_graph=steps)
     ops = 2 * 2048 * sum(M * K for M, K in wl.shapes)
     kt, launches = kernel_pass(m, steps)
     per_launch_ops = ops / 4
