@@ -5,7 +5,9 @@
 // the codes 0/1/2 directly: sum_k (code - 1) * xq = sum_k code * xq - sum xq.
 //
 // One workgroup per token and input (several inputs of the same tokens can
-// share one launch).  Rows of up to 8 * threads * C elements are done
+// share one launch), of 128, 256 or 512 threads: the fewest that keep the
+// longest row within 8 chunks per thread (small workgroups turn over faster
+// when there are thousands of rows).  Rows of up to 8 * threads * C elements are done
 // in one pass: every thread loads all of its C chunks of 8 elements at once
 // (no load waits on another), the absmax is reduced in registers, across the
 // wave with DPP moves and across the waves through LDS, and the codes are
@@ -19,24 +21,25 @@ namespace bt {
 
 namespace {
 
-constexpr int kQuantThreads = 512;
+constexpr int kQuantThreads = 512;  // two-pass kernel, and the one-pass maximum
 constexpr int kQuantWaves = kQuantThreads / kWave;
 
 // Max over the waves' partial maxima / sums written to LDS (after a barrier).
-template <bool MAX>
-__device__ __forceinline__ uint32_t across_waves(const uint32_t (&part)[kQuantWaves]) {
+template <bool MAX, int W>
+__device__ __forceinline__ uint32_t across_waves(const uint32_t (&part)[W]) {
     uint32_t v = part[0];
 #pragma unroll
-    for (int w = 1; w < kQuantWaves; ++w) v = MAX ? max(v, part[w]) : v + part[w];
+    for (int w = 1; w < W; ++w) v = MAX ? max(v, part[w]) : v + part[w];
     return v;
 }
 
-// One-pass quantization of token blockIdx.x of input blockIdx.y.
-template <typename T, int C>
-__global__ __launch_bounds__(kQuantThreads)
+// One-pass quantization of token blockIdx.x of input blockIdx.y, TH threads.
+template <typename T, int C, int TH>
+__global__ __launch_bounds__(TH)
 void quant_onepass_kernel(QuantJobs jobs) {
-    __shared__ uint32_t red_m[kQuantWaves];
-    __shared__ uint32_t red_s[kQuantWaves];
+    constexpr int kWaves = TH / kWave;
+    __shared__ uint32_t red_m[kWaves];
+    __shared__ uint32_t red_s[kWaves];
     const int64_t n = blockIdx.x;
     const int job = __builtin_amdgcn_readfirstlane(blockIdx.y);
     const T *x = static_cast<const T *>(jobs.x[0]);
@@ -63,7 +66,7 @@ void quant_onepass_kernel(QuantJobs jobs) {
     Raw8<T> raw[C];
 #pragma unroll
     for (int c = 0; c < C; ++c)
-        raw[c].load(row + min(8 * ((int64_t)threadIdx.x + (int64_t)c * kQuantThreads), K - 8));
+        raw[c].load(row + min(8 * ((int64_t)threadIdx.x + (int64_t)c * TH), K - 8));
     uint32_t m = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c)  // re-read chunks cannot change a max
@@ -76,7 +79,7 @@ void quant_onepass_kernel(QuantJobs jobs) {
     int sum = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const int64_t k = 8 * ((int64_t)threadIdx.x + (int64_t)c * kQuantThreads);
+        const int64_t k = 8 * ((int64_t)threadIdx.x + (int64_t)c * TH);
         int part = 0;
         const uint2 q = quant8(raw[c].eight(), inv, part);
         if (k < K) {
@@ -134,19 +137,27 @@ void quant_twopass_kernel(const T *__restrict__ x, int64_t K, int8_t *__restrict
 // All jobs in one launch when every row fits the one-pass kernel (the chunk
 // count is that of the longest row; shorter rows mask the extra chunks),
 // else one two-pass launch per job.
+template <typename T, int TH>
+void launch_onepass(const QuantJobs &jobs, int64_t chunks, dim3 grid, hipStream_t s) {
+    const dim3 block(TH);
+    if (chunks <= 1) hipLaunchKernelGGL((quant_onepass_kernel<T, 1, TH>), grid, block, 0, s, jobs);
+    else if (chunks <= 2) hipLaunchKernelGGL((quant_onepass_kernel<T, 2, TH>), grid, block, 0, s, jobs);
+    else if (chunks <= 4) hipLaunchKernelGGL((quant_onepass_kernel<T, 4, TH>), grid, block, 0, s, jobs);
+    else hipLaunchKernelGGL((quant_onepass_kernel<T, 8, TH>), grid, block, 0, s, jobs);
+}
+
 template <typename T>
 hipError_t launch_quant_t(const QuantJobs &jobs, int count, int64_t N, hipStream_t s) {
     int64_t kmax = 0;
     for (int i = 0; i < count; ++i) kmax = max(kmax, jobs.K[i]);
-    const int64_t chunks = (kmax / 8 + kQuantThreads - 1) / kQuantThreads;  // per thread
-    const dim3 grid((unsigned)N, (unsigned)count), block(kQuantThreads);
-    if (chunks <= 1) hipLaunchKernelGGL((quant_onepass_kernel<T, 1>), grid, block, 0, s, jobs);
-    else if (chunks <= 2) hipLaunchKernelGGL((quant_onepass_kernel<T, 2>), grid, block, 0, s, jobs);
-    else if (chunks <= 4) hipLaunchKernelGGL((quant_onepass_kernel<T, 4>), grid, block, 0, s, jobs);
-    else if (chunks <= 8) hipLaunchKernelGGL((quant_onepass_kernel<T, 8>), grid, block, 0, s, jobs);
+    const int64_t units = kmax / 8;  // 8-element chunks of the longest row
+    const dim3 grid((unsigned)N, (unsigned)count);
+    if (units <= 128 * 8) launch_onepass<T, 128>(jobs, (units + 127) / 128, grid, s);
+    else if (units <= 256 * 8) launch_onepass<T, 256>(jobs, (units + 255) / 256, grid, s);
+    else if (units <= 512 * 8) launch_onepass<T, 512>(jobs, (units + 511) / 512, grid, s);
     else
         for (int i = 0; i < count; ++i)
-            hipLaunchKernelGGL(quant_twopass_kernel<T>, dim3((unsigned)N), block, 0, s,
+            hipLaunchKernelGGL(quant_twopass_kernel<T>, dim3((unsigned)N), dim3(kQuantThreads), 0, s,
                                static_cast<const T *>(jobs.x[i]), jobs.K[i], jobs.xq[i], jobs.xs[i],
                                jobs.xsum[i]);
     return hipGetLastError();
