@@ -28,6 +28,16 @@ struct LayerArgs {
     int k32[kLayerInputs];
     int xoff32[kLayerInputs];
     int qb32[kLayerInputs];  // 256-column blocks per row
+    // Work schedule over tile groups (the tiles one iteration of a workgroup
+    // takes together).  sched = 0: workgroup w takes groups w, w + G, ...
+    // sched = 1 (set by the launcher when it balances better): groups
+    // [0, ts) are the light ones, [ts, end) the heavy ones; workgroups
+    // [0, n0) form class 0, the rest class 1; a class-c workgroup takes an
+    // even share of its class's scount[c] light groups (from sstart[c]) and
+    // then heavy[c] heavy groups (class 0 from ts, class 1 from
+    // ts + n0 * heavy[0]).
+    int sched, n0, ts;
+    int heavy[2], sstart[2], scount[2];
 };
 
 // Whether one launch can run the block: 1..4 tokens, every K at least one
