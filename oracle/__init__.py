@@ -10,7 +10,8 @@ arrays through ctypes.  The readings of the pages it follows are listed in the
 header of that file.  The float -> ternary weight quantizer (AbsMean and
 max|w| scales, RoundClip) is ``weight_quant.py``: numpy plus exact Python
 integer arithmetic, its readings in its own header.  Dequantization
-(to_float) and the I2_S byte layout are ``interop.py`` (numpy).
+(to_float) and the I2_S byte layout are ``interop.py`` (numpy).  The denser
+base-3 packing (64 weights in 13 bytes) is ``base3.py`` (numpy).
 
 Sources, cited by page title and section:
   [I2S]  "How BitNet's 1-Bit (I2_S) Quantization Works Compared to Standard
