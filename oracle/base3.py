@@ -22,8 +22,12 @@ into tiles of 16 rows x 1024 columns, tile (m/16, k/1024) at byte offset
 ((m/16) * (K/1024) + k/1024) * 3328.  Lane l = r + 16 s (r = m % 16, s =
 (k % 1024) / 256) owns the 4 blocks (52 bytes, 13 little-endian 32-bit words)
 of row r, columns 256 s .. 256 s + 255 of the tile, block b = columns
-256 s + 64 b ..; byte i of its 52 is block i // 13, byte i % 13.  Word d of
-lane l sits at tile offset (64 d + l) * 4.  The float32 scale follows the
+256 s + 64 b .. 256 s + 64 b + 63.  Words 3b, 3b+1, 3b+2 hold bytes 0..11 of
+block b (byte j in word 3b + j // 4 at byte j % 4); word 12 holds byte 12 of
+block b at its byte b.  Word d < 12 of lane l sits at tile offset
+16 (64 (d // 4) + l) + 4 (d % 4) -- so words 0..11 are three 16-byte chunks
+that a 64-lane wave reads with three fully coalesced 128-bit loads -- and
+word 12 at tile offset 3072 + 4 l.  The float32 scale follows the
 M * K * 13 / 64 code bytes, then zeros up to 256 tail bytes.
 """
 from __future__ import annotations
@@ -65,8 +69,9 @@ def decode_block(b: np.ndarray) -> np.ndarray:
 
 
 def _lane_runs(M: int, K: int, rows=None):
-    """(row, first column, byte offsets of the 52 run bytes) of every lane
-    (of the given rows only, if rows is not None)."""
+    """(row, first column, byte offsets of the 52 bytes of the lane's four
+    blocks in block order) of every lane (of the given rows only, if rows is
+    not None)."""
     qt = K // TILE_COLS
     keep = None if rows is None else set(int(r) for r in rows)
     for mt in range(M // TILE_ROWS):
@@ -76,7 +81,13 @@ def _lane_runs(M: int, K: int, rows=None):
                 r, s = lane % 16, lane // 16
                 if keep is not None and mt * TILE_ROWS + r not in keep:
                     continue
-                offs = [base + (64 * (i // 4) + lane) * 4 + i % 4 for i in range(52)]
+                offs = []
+                for b in range(4):       # run byte 13 b + j = byte j of block b
+                    for j in range(13):
+                        d, t = (3 * b + j // 4, j % 4) if j < 12 else (12, b)
+                        word = 16 * (64 * (d // 4) + lane) + 4 * (d % 4) if d < 12 \
+                            else 3072 + 4 * lane
+                        offs.append(base + word + t)
                 yield mt * TILE_ROWS + r, q * TILE_COLS + 256 * s, offs
 
 

@@ -59,9 +59,19 @@ def test_weight_positions():
         lane = m % 16 + 16 * ((k % 1024) // 256)
         blk, col = (k % 256) // 64, k % 64
         j = col // 4 if col < 48 else (col - 48 if col < 60 else 12)
-        i = 13 * blk + j
-        off = tile * 3328 + (64 * (i // 4) + lane) * 4 + i % 4
+        if j < 12:   # word 3 blk + j // 4: chunk (3 blk + j // 4) // 4 of the lane
+            word = 3 * blk + j // 4
+            off = tile * 3328 + 16 * (64 * (word // 4) + lane) + 4 * (word % 4) + j % 4
+        else:        # word 12, byte blk
+            off = tile * 3328 + 3072 + 4 * lane + blk
         assert diff.tolist() == [off], (m, k)
+
+
+def test_code_bytes_are_a_partition():
+    # every byte of the code region belongs to exactly one lane's block byte
+    M, K = 32, 2048
+    offs = np.concatenate([np.asarray(o) for _, _, o in b3._lane_runs(M, K)])
+    assert np.array_equal(np.sort(offs), np.arange(M * K * 13 // 64))
 
 
 @pytest.mark.parametrize("M,K", [(16, 1024), (48, 2048), (32, 3072)])
