@@ -390,6 +390,54 @@ def weight_quant_extra(steps, warmup):
     return res
 
 
+def base3_extra(steps, warmup, use_graph, layers=8):
+    """The 70B-class block's seven matrices in both weight formats, one
+    decode launch per matrix on activations quantized beforehand, `layers`
+    blocks deep so that the weights stream from HBM rather than from the
+    last-level cache: the 2-bit T16Q256 kernel against the base-3 B3T1024
+    one (1.625 bits per weight), at 1 and 4 tokens."""
+    import torch
+    import ternary_weight_quantized_bt_amd as bt
+    import workloads as W
+    dev = "cuda:0"
+    shapes = W.STREAM70B.shapes
+    mats = []
+    for l in range(layers):
+        for i, (M, K) in enumerate(shapes):
+            w = W.ternary_weights(M, K, "p0_0.4", 7000 + 10 * l + i, device=dev)
+            mats.append((M, K, bt.pack(w, 0.02), bt.pack_b3(w, 0.02)))
+            del w
+    weights = layers * sum(M * K for M, K in shapes)
+    fmt_bytes = {"t16q256_2bit": sum(m[2].numel() for m in mats),
+                 "b3t1024_base3": sum(m[3].numel() for m in mats)}
+    res = {"layers": layers, "launches_per_step": len(mats),
+           "packed_gb": {k: round(v / 1e9, 3) for k, v in fmt_bytes.items()}}
+    for N in (1, 4):
+        acts = {K: bt.quant_act(W.activations(N, K, "normal", K + N, "bf16", device=dev))
+                for K in sorted({K for _, K in shapes})}
+        outs = {M: torch.empty((N, M), dtype=torch.bfloat16, device=dev)
+                for M in sorted({M for M, _ in shapes})}
+        row = {}
+        for name, which, fn in (("t16q256_2bit", 2, bt.bt_ternary_gemv),
+                                ("b3t1024_base3", 3, bt.bt_ternary_gemv_b3)):
+            def step():
+                for m in mats:
+                    M, K = m[0], m[1]
+                    xq, xsc, xsm = acts[K]
+                    fn(m[which], M, K, xq, xsc, xsm, N, outs[M], bt.BT_BF16)
+            sec, _ = run_steps(None, steps, warmup, use_graph, step=step)
+            row[name] = {"ms_per_step": round(sec * 1e3, 4),
+                         "packed_gb_per_s": round(fmt_bytes[name] / sec / 1e9, 1),
+                         "frac_of_hbm_peak": round(fmt_bytes[name] / sec / 1e9 / PEAK_HBM_GBS, 4),
+                         "t_weights_per_s": round(weights / sec / 1e12, 2)}
+        row["base3_over_2bit_weights_per_s"] = round(
+            row["b3t1024_base3"]["t_weights_per_s"] / row["t16q256_2bit"]["t_weights_per_s"], 3)
+        res[f"{N}_token" + ("s" if N > 1 else "")] = row
+    del mats
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -507,6 +555,7 @@ def main():
         torch.cuda.empty_cache()
         extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
         extra["weight_quantizer_70b_gate"] = weight_quant_extra(args.steps, args.warmup)
+        extra["base3_vs_2bit_70b"] = base3_extra(args.steps, args.warmup, use_graph)
 
     cpu = None
     if not args.no_cpu:

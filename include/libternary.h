@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 4
+#define BT_ABI_VERSION 5
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -186,6 +186,53 @@ bt_status bt_i2s_import(const uint8_t *i2s, int64_t M, int64_t K, int64_t block,
 
 bt_status bt_i2s_export(const uint8_t *packed, int64_t M, int64_t K,
                         int64_t block, uint8_t *i2s, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Denser base-3 weight format "B3T1024", 1.625 bits per weight ([IK]
+ * sections 5.2, 5.3 and 6: a ternary format of that density over blocks of
+ * 64 weights, decoded with integer arithmetic instead of 2-bit masks).  The
+ * pages fix the density and the block; the bytes are this library's:
+ *   codes c = W + 1; the 64 weights of row m, columns 64i .. 64i+63 are 13
+ *   bytes: byte j < 12 = c[4j] + 3c[4j+1] + 9c[4j+2] + 27c[4j+3] + 81c[48+j]
+ *   (0..242) and byte 12 = c[60] + 3c[61] + 9c[62] + 27c[63] (0..80), with
+ *   c[t] the code of column 64i + t.
+ *   Tiles of 16 rows x 1024 columns, 3328 bytes each; tile (m/16, k/1024)
+ *   starts at ((m/16)*(K/1024) + k/1024) * 3328.  Lane l = (m%16) +
+ *   16*((k%1024)/256) of a tile holds the four blocks b = 0..3 of row m%16,
+ *   columns 256*(l/16) + 64b .. of the tile, as 13 32-bit words: words
+ *   3b .. 3b+2 hold bytes 0..11 of block b (byte j at word 3b + j/4, byte
+ *   j%4) and byte b of word 12 holds byte 12 of block b.  Word d < 12 of lane
+ *   l is at tile offset 16*(64*(d/4) + l) + 4*(d%4); word 12 is at
+ *   3072 + 4*l.  (A 64-lane wave reads a tile with three 128-bit and one
+ *   32-bit coalesced load.)  The float32 scale follows at byte M*K*13/64,
+ *   then zeros up to BT_TAIL_BYTES tail bytes.
+ * Shapes: M % 16 == 0, K % 1024 == 0, 0 < K <= BT_MAX_K.  Code bytes other
+ * than the ones bt_pack_ternary_b3 writes (a byte above 242, or byte 12
+ * above 80) are outside the contract.
+ *
+ * bt_b3_bytes: M*K*13/64 + BT_TAIL_BYTES, or 0 if the shape is not
+ *   supported.
+ * bt_pack_ternary_b3 / bt_unpack_ternary_b3: as bt_pack_ternary /
+ *   bt_unpack_ternary (clamping and counting of values outside {-1,0,+1}
+ *   included) for this layout.
+ * bt_ternary_gemv_b3: the product of bt_ternary_gemv over B3T1024 weights,
+ *   with identical results (the same exact int32 sums and the same float32
+ *   dequantization).  Tokens are processed four at a time; every four
+ *   tokens stream the weights once.
+ * ---------------------------------------------------------------------- */
+size_t bt_b3_bytes(int64_t M, int64_t K);
+
+bt_status bt_pack_ternary_b3(const int8_t *w, int64_t M, int64_t K, float scale,
+                             uint8_t *packed, int32_t *invalid_count,
+                             bt_stream stream);
+
+bt_status bt_unpack_ternary_b3(const uint8_t *packed, int64_t M, int64_t K,
+                               int8_t *w, bt_stream stream);
+
+bt_status bt_ternary_gemv_b3(const uint8_t *packed, int64_t M, int64_t K,
+                             const int8_t *xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t N,
+                             void *y, bt_dtype y_dtype, bt_stream stream);
 
 /* ------------------------------------------------------------------------
  * Per-token absmax int8 activation quantization ([PARA] section 5, Quant8).

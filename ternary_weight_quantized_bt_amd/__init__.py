@@ -83,7 +83,7 @@ BT_WSCALE_ABSMAX = 1
 BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 
@@ -121,6 +121,14 @@ def lib() -> ctypes.CDLL:
         L.bt_i2s_import.restype = S
         L.bt_i2s_export.argtypes = [P, I64, I64, I64, P, P]
         L.bt_i2s_export.restype = S
+        L.bt_b3_bytes.argtypes = [I64, I64]
+        L.bt_b3_bytes.restype = ctypes.c_size_t
+        L.bt_pack_ternary_b3.argtypes = [P, I64, I64, ctypes.c_float, P, P, P]
+        L.bt_pack_ternary_b3.restype = S
+        L.bt_unpack_ternary_b3.argtypes = [P, I64, I64, P, P]
+        L.bt_unpack_ternary_b3.restype = S
+        L.bt_ternary_gemv_b3.argtypes = [P, I64, I64, P, P, P, I64, P, S, P]
+        L.bt_ternary_gemv_b3.restype = S
         L.bt_quantize_weights_workspace_bytes.argtypes = []
         L.bt_quantize_weights_workspace_bytes.restype = ctypes.c_size_t
         L.bt_quantize_weights.argtypes = [P, S, I64, I64, S, ctypes.c_float, P, P, P,
@@ -213,6 +221,24 @@ def bt_i2s_export(packed, M, K, block, i2s, stream=None):
     _check(lib().bt_i2s_export(_p(packed), M, K, block, _p(i2s), _stream(stream)))
 
 
+def bt_b3_bytes(M: int, K: int) -> int:
+    return lib().bt_b3_bytes(M, K)
+
+
+def bt_pack_ternary_b3(w, M, K, scale, packed, invalid_count=None, stream=None):
+    _check(lib().bt_pack_ternary_b3(_p(w), M, K, float(scale), _p(packed),
+                                    _p(invalid_count), _stream(stream)))
+
+
+def bt_unpack_ternary_b3(packed, M, K, w, stream=None):
+    _check(lib().bt_unpack_ternary_b3(_p(packed), M, K, _p(w), _stream(stream)))
+
+
+def bt_ternary_gemv_b3(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype, stream=None):
+    _check(lib().bt_ternary_gemv_b3(_p(packed), M, K, _p(xq), _p(x_scale), _p(x_sum),
+                                    N, _p(y), y_dtype, _stream(stream)))
+
+
 def bt_quantize_weights_workspace_bytes() -> int:
     return lib().bt_quantize_weights_workspace_bytes()
 
@@ -288,6 +314,23 @@ def unpack(packed: torch.Tensor, M: int, K: int, stream=None):
     return w
 
 
+def pack_b3(w: torch.Tensor, scale: float, invalid_count=None, stream=None):
+    """int8 [M, K] device tensor -> base-3 B3T1024 packed uint8 device tensor."""
+    M, K = w.shape
+    n = bt_b3_bytes(M, K)
+    if n == 0:
+        raise BtError(BT_ERR_SHAPE, bt_last_error())
+    packed = torch.empty(n, dtype=torch.uint8, device=w.device)
+    bt_pack_ternary_b3(w, M, K, scale, packed, invalid_count, stream)
+    return packed
+
+
+def unpack_b3(packed: torch.Tensor, M: int, K: int, stream=None):
+    w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
+    bt_unpack_ternary_b3(packed, M, K, w, stream)
+    return w
+
+
 def dequantize(packed: torch.Tensor, M: int, K: int, dtype=torch.float32, stream=None):
     """Packed weights -> float32 / bfloat16 [M, K] device tensor
     ((code - 1) * scale)."""
@@ -359,6 +402,11 @@ def _matmul(fn, packed, M, K, xq, xs, xsum, y_dtype, stream):
 
 def gemv(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
     return _matmul(bt_ternary_gemv, packed, M, K, xq, xs, xsum, y_dtype, stream)
+
+
+def gemv_b3(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
+    """The decode product over base-3 B3T1024 weights (same results as gemv)."""
+    return _matmul(bt_ternary_gemv_b3, packed, M, K, xq, xs, xsum, y_dtype, stream)
 
 
 def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):

@@ -213,6 +213,51 @@ bt_status bt_i2s_export(const uint8_t *packed, int64_t M, int64_t K, int64_t blo
     return hip_status(bt::launch_i2s_export(packed, M, K, block, i2s, as_stream(stream)), fn);
 }
 
+static bt_status check_b3(int64_t M, int64_t K, const char *fn) {
+    BT_TRY(check_mk(M, K, fn));
+    if (K % 1024 != 0)
+        return fail(BT_ERR_SHAPE, "%s: K=%lld is not a multiple of 1024", fn, (long long)K);
+    return BT_OK;
+}
+
+size_t bt_b3_bytes(int64_t M, int64_t K) {
+    if (check_b3(M, K, "bt_b3_bytes") != BT_OK) return 0;
+    ok();
+    return (size_t)(M * K / 64 * 13) + BT_TAIL_BYTES;
+}
+
+bt_status bt_pack_ternary_b3(const int8_t *w, int64_t M, int64_t K, float scale,
+                             uint8_t *packed, int32_t *invalid_count, bt_stream stream) {
+    const char *fn = "bt_pack_ternary_b3";
+    BT_TRY(check_b3(M, K, fn));
+    BT_TRY(check_ptr(w, "w", fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (invalid_count && (reinterpret_cast<uintptr_t>(invalid_count) & 3u))
+        return fail(BT_ERR_ALIGN, "%s: invalid_count not 4-byte aligned", fn);
+    return hip_status(bt::launch_b3_pack(w, M, K, scale, packed, invalid_count,
+                                         as_stream(stream)), fn);
+}
+
+bt_status bt_unpack_ternary_b3(const uint8_t *packed, int64_t M, int64_t K, int8_t *w,
+                               bt_stream stream) {
+    const char *fn = "bt_unpack_ternary_b3";
+    BT_TRY(check_b3(M, K, fn));
+    BT_TRY(check_ptr(packed, "packed", fn));
+    BT_TRY(check_ptr(w, "w", fn));
+    return hip_status(bt::launch_b3_unpack(packed, M, K, w, as_stream(stream)), fn);
+}
+
+bt_status bt_ternary_gemv_b3(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,
+                             const float *x_scale, const int32_t *x_sum, int64_t N, void *y,
+                             bt_dtype y_dtype, bt_stream stream) {
+    const char *fn = "bt_ternary_gemv_b3";
+    BT_TRY(check_b3(M, K, fn));
+    BT_TRY(check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, y, y_dtype));
+    if (N == 0) return ok();
+    return hip_status(bt::launch_b3_gemv(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype,
+                                         as_stream(stream)), fn);
+}
+
 size_t bt_quantize_weights_workspace_bytes(void) { return BT_WQ_WORKSPACE_BYTES; }
 
 bt_status bt_quantize_weights(const void *w, bt_dtype w_dtype, int64_t M, int64_t K,

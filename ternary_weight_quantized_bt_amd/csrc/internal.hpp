@@ -19,6 +19,14 @@ hipError_t launch_i2s_import(const uint8_t *src, int64_t M, int64_t K, int64_t b
                              uint8_t *packed, int32_t *invalid, hipStream_t s);
 hipError_t launch_i2s_export(const uint8_t *packed, int64_t M, int64_t K, int64_t block,
                              uint8_t *dst, hipStream_t s);
+// Base-3 "B3T1024" weights: packing, unpacking, decode product (any N).
+hipError_t launch_b3_pack(const int8_t *w, int64_t M, int64_t K, float scale, uint8_t *packed,
+                          int32_t *invalid, hipStream_t s);
+hipError_t launch_b3_unpack(const uint8_t *packed, int64_t M, int64_t K, int8_t *w,
+                            hipStream_t s);
+hipError_t launch_b3_gemv(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,
+                          const float *xs, const int32_t *xsum, int64_t N, void *y,
+                          bt_dtype ydt, hipStream_t s);
 // Float -> packed ternary weights (workspace: BT_WQ_WORKSPACE_BYTES).
 hipError_t launch_quantize_weights(const void *w, bt_dtype wdt, int64_t M, int64_t K, int mode,
                                    float eps, uint8_t *packed, float *stats, void *workspace,

@@ -23,6 +23,8 @@ def test_header_declares_the_boundary():
     for n in ("bt_pack_ternary", "bt_unpack_ternary", "bt_quant_act",
               "bt_quantize_weights", "bt_quantize_weights_workspace_bytes",
               "bt_dequantize_weights", "bt_i2s_import", "bt_i2s_export", "bt_i2s_bytes",
+              "bt_b3_bytes", "bt_pack_ternary_b3", "bt_unpack_ternary_b3",
+              "bt_ternary_gemv_b3",
               "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
               "bt_layer_workspace_bytes", "bt_packed_bytes", "bt_last_error",
               "bt_abi_version"):
@@ -39,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 4
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 5
 
 
 def test_packed_bytes():
@@ -152,6 +154,35 @@ def test_quantize_weights_workspace_bytes():
     ("bt_i2s_export", (A, 16, 256, 4, None), bt.BT_ERR_INVALID_ARG),
 ])
 def test_interop_validation(fn, args, status):
+    with pytest.raises(bt.BtError) as e:
+        getattr(bt, fn)(*args, stream=0)
+    assert e.value.status == status
+
+
+def test_b3_bytes():
+    assert bt.bt_b3_bytes(16, 1024) == 16 * 1024 * 13 // 64 + 256
+    assert bt.bt_b3_bytes(8192, 28672) == 8192 * 28672 * 13 // 64 + 256
+    assert bt.bt_b3_bytes(16, 768) == 0
+    assert "multiple of 1024" in bt.bt_last_error()
+    assert bt.bt_b3_bytes(8, 1024) == 0
+    assert bt.bt_b3_bytes(16, 132096) == 0  # above BT_MAX_K
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    ("bt_pack_ternary_b3", (A, 16, 512, 1.0, A), bt.BT_ERR_SHAPE),
+    ("bt_pack_ternary_b3", (A, 15, 1024, 1.0, A), bt.BT_ERR_SHAPE),
+    ("bt_pack_ternary_b3", (None, 16, 1024, 1.0, A), bt.BT_ERR_INVALID_ARG),
+    ("bt_pack_ternary_b3", (A, 16, 1024, 1.0, A + 4), bt.BT_ERR_ALIGN),
+    ("bt_pack_ternary_b3", (A, 16, 1024, 1.0, A, A + 2), bt.BT_ERR_ALIGN),
+    ("bt_unpack_ternary_b3", (A, 16, 2560, A), bt.BT_ERR_SHAPE),
+    ("bt_unpack_ternary_b3", (A, 16, 1024, None), bt.BT_ERR_INVALID_ARG),
+    ("bt_ternary_gemv_b3", (A, 16, 256, A, A, A, 1, A, bt.BT_F32), bt.BT_ERR_SHAPE),
+    ("bt_ternary_gemv_b3", (A, 16, 1024, A, A, A, -1, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ("bt_ternary_gemv_b3", (A, 16, 1024, A, A, A, 1, A, 7), bt.BT_ERR_DTYPE),
+    ("bt_ternary_gemv_b3", (A, 16, 1024, None, A, A, 1, A, bt.BT_F32), bt.BT_ERR_INVALID_ARG),
+    ("bt_ternary_gemv_b3", (A, 16, 1024, A, A, A, 1, A + 8, bt.BT_F32), bt.BT_ERR_ALIGN),
+])
+def test_b3_validation(fn, args, status):
     with pytest.raises(bt.BtError) as e:
         getattr(bt, fn)(*args, stream=0)
     assert e.value.status == status
