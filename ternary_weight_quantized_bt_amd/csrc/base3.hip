@@ -315,12 +315,16 @@ void b3_gemv_kernel(B3Args a) {
     }
 
     // ---- prologue: the table, the activations, the per-token constants ----
+    // Thread t computes entry v = t / 4 once and writes copies 8 (t % 4) ..
+    // 8 (t % 4) + 7: 64 contiguous bytes at v * 256 + 64 (t % 4).
     uint8_t *tab = b3_smem;
-    for (int idx = threadIdx.x; idx < 256 * kB3Copies; idx += kThreads) {
-        const uint32_t v = (uint32_t)idx / kB3Copies;
-        uint2 e = {0u, 0u};
-        if (v < 243) e = uint2{low_digits(v), (v / 81) * 0x01010101u};
-        reinterpret_cast<uint2 *>(tab)[idx] = e;  // byte v * 256 + 8 (idx % 32)
+    for (int t = threadIdx.x; t < 256 * 4; t += kThreads) {
+        const uint32_t v = (uint32_t)t / 4;
+        const uint32_t lo = v < 243 ? low_digits(v) : 0u;
+        const uint32_t hi = v < 243 ? (v / 81) * 0x01010101u : 0u;
+        v4u *dst = reinterpret_cast<v4u *>(tab + 64 * t);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = v4u{lo, hi, lo, hi};
     }
     const int8_t *xsrc = a.xq;
     if (LDSX) {
@@ -409,10 +413,6 @@ void b3_gemv_kernel(B3Args a) {
     }
 }
 
-// 16 waves per workgroup for one or two tokens, 8 for four (more registers
-// per lane for the accumulators and activation words).
-template <int NT>
-constexpr int b3_waves() { return NT == 4 ? 8 : 16; }
 constexpr int kB3Ring = 2;
 
 // Static LDS of b3_gemv_kernel (the reduction buffers, per-token constants).
@@ -434,11 +434,10 @@ int max_lds_per_block() {
     return lds[dev];
 }
 
-template <int NT, bool LDSX, int P>
+template <int NT, bool LDSX, int WAVES, int P>
 hipError_t launch_b3_p(const B3Args &a, size_t shmem, hipStream_t s) {
-    constexpr int kWaves = b3_waves<NT>();
-    constexpr int TPW = kWaves / P;
-    auto kern = b3_gemv_kernel<NT, LDSX, kWaves, P, kB3Ring>;
+    constexpr int TPW = WAVES / P;
+    auto kern = b3_gemv_kernel<NT, LDSX, WAVES, P, kB3Ring>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)shmem);
@@ -447,18 +446,37 @@ hipError_t launch_b3_p(const B3Args &a, size_t shmem, hipStream_t s) {
     const int per_cu = (int)max((size_t)1, min((size_t)2, (size_t)max_lds_per_cu() /
                                                           (shmem + b3_static_lds(NT))));
     const int64_t grid = min(groups, (int64_t)device_cus() * per_cu);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWaves * kWave), shmem, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * kWave), shmem, s, a);
     return hipGetLastError();
 }
 
-// K split: the most waves per row tile (up to 8) that each get a tile column.
+// Launch shape.  Every iteration of a workgroup ends in a cross-wave
+// reduction and a barrier that cost about as much as streaming two or three
+// tiles, so iterations should be few and long:
+//   - enough row tiles to give three quarters of the compute units a group
+//     of 8, and LDS for two workgroups per unit: 8 waves that each own a
+//     whole row tile (no K split, no barrier);
+//   - otherwise 16 waves (8 for four tokens: registers), split along K into
+//     the fewest parts P that still give every compute unit a workgroup, at
+//     most 8 and at most one part per tile column.
 template <int NT, bool LDSX>
 hipError_t launch_b3_x(const B3Args &a, size_t shmem, hipStream_t s) {
-    const int64_t qc = a.K / kB3Cols;
-    if (qc >= 8) return launch_b3_p<NT, LDSX, 8>(a, shmem, s);
-    if (qc >= 4) return launch_b3_p<NT, LDSX, 4>(a, shmem, s);
-    if (qc >= 2) return launch_b3_p<NT, LDSX, 2>(a, shmem, s);
-    return launch_b3_p<NT, LDSX, 1>(a, shmem, s);
+    const int64_t mtiles = a.M / kTileRows, qc = a.K / kB3Cols;
+    const int64_t cus = device_cus();
+    const bool two_per_cu = 2 * (shmem + b3_static_lds(NT)) <= (size_t)max_lds_per_cu();
+    if (two_per_cu && (mtiles + 7) / 8 * 4 >= 3 * cus)
+        return launch_b3_p<NT, LDSX, 8, 1>(a, shmem, s);
+    constexpr int W = NT == 4 ? 8 : 16;
+    int pmax = 1;
+    while (pmax < 8 && 2 * pmax <= qc) pmax *= 2;
+    int P = 1;
+    while (P < pmax && (mtiles + W / P - 1) / (W / P) < cus) P *= 2;
+    switch (P) {
+        case 1: return launch_b3_p<NT, LDSX, W, 1>(a, shmem, s);
+        case 2: return launch_b3_p<NT, LDSX, W, 2>(a, shmem, s);
+        case 4: return launch_b3_p<NT, LDSX, W, 4>(a, shmem, s);
+        default: return launch_b3_p<NT, LDSX, W, 8>(a, shmem, s);
+    }
 }
 
 template <int NT>

@@ -83,6 +83,24 @@ def test_gemv_int32_exact(M, K):
         assert_equal(to_np(y), ref["acc"], f"B3 gemv M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K", [(32768, 1024), (32768, 3072)])
+def test_gemv_tall_matrices_whole_row_tiles(M, K):
+    # 2048 row tiles: enough for the shape in which every wave owns whole row
+    # tiles (no K split, no cross-wave reduction); the weights are packed on
+    # the GPU (their bytes are pinned to the oracle's above) and every output
+    # is compared with the oracle's product
+    w = W.ternary_weights(M, K, "p0_0.4", M + K)
+    ref2, _ = oracle.pack(w.numpy(), 0.025)
+    packed = bt.pack_b3(w.to(DEV), 0.025)
+    for N in (1, 2, 3, 4, 5):
+        print(f"b3 gemv tall {M}x{K} N={N}", flush=True)
+        ref, xq, xs, xsum = _tokens(ref2, M, K, N, 3 * N + K)
+        y = bt.gemv_b3(packed, M, K, xq, xs, xsum, bt.BT_I32)
+        assert_equal(to_np(y), ref["acc"], f"B3 gemv M={M} K={K} N={N}")
+        y = bt.gemv_b3(packed, M, K, xq, xs, xsum, bt.BT_BF16)
+        assert_rel_close(as_f64(y), ref["y"], RTOL[bt.BT_BF16], f"B3 gemv bf16 N={N}")
+
+
 @pytest.mark.parametrize("ydt", [bt.BT_F32, bt.BT_BF16])
 def test_gemv_float_within_tolerance(ydt):
     for (M, K, N) in [(48, 2048, 1), (80, 3072, 2), (1040, 8192, 4), (32, 4096, 7)]:

@@ -1,7 +1,7 @@
 """Pins of the oracle's base-3 packing (64 weights in 13 bytes, layout
 B3T1024): hand-worked blocks, exhaustive digit round trips, the byte
 position of every weight by an independent formula, whole-matrix round
-trips, and the multiply-shift division the GPU decoder uses."""
+trips."""
 import numpy as np
 import pytest
 
@@ -94,10 +94,3 @@ def test_bad_shapes_and_values():
         b3.packed_bytes(16, 512)
     with pytest.raises(ValueError):
         b3.pack(np.full((16, 1024), 2, np.int8), 1.0)
-
-
-def test_multiply_shift_fifth_digit():
-    # the GPU decoder takes the fifth digit v // 81 as (v * 810) >> 16;
-    # exact for every byte the encoding writes (0..242)
-    v = np.arange(243)
-    assert np.array_equal((v * 810) >> 16, v // 81)
