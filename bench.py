@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB, five times "
                          "(reference for the HBM traffic counters)")
+    ap.add_argument("--base3-only", action="store_true",
+                    help="only compare the 2-bit and base-3 weight formats on the "
+                         "70B-class matrices (--layers blocks deep, default 8)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
                     help="no GPU: read four rocprofv3 --pmc output folders (copy "
                          "FETCH_SIZE, copy WRITE_SIZE, step FETCH_SIZE, step "
@@ -435,6 +438,29 @@ def base3_extra(steps, warmup, use_graph, layers=8):
         res[f"{N}_token" + ("s" if N > 1 else "")] = row
     del mats
     torch.cuda.empty_cache()
+    # Steady state: one tall matrix per launch (229376 x 8192, 1.9 G weights),
+    # so that launch and prologue costs are amortized.
+    M, K = 229376, 8192
+    w = W.ternary_weights(M, K, "p0_0.4", 7777, device=dev)
+    tall = {"t16q256_2bit": (bt.pack(w, 0.02), bt.bt_ternary_gemv),
+            "b3t1024_base3": (bt.pack_b3(w, 0.02), bt.bt_ternary_gemv_b3)}
+    del w
+    xq, xsc, xsm = bt.quant_act(W.activations(1, K, "normal", 5, "bf16", device=dev))
+    y = torch.empty((1, M), dtype=torch.bfloat16, device=dev)
+    row = {"shape": [M, K], "tokens": 1}
+    for name, (p, fn) in tall.items():
+        def step():
+            fn(p, M, K, xq, xsc, xsm, 1, y, bt.BT_BF16)
+        sec, _ = run_steps(None, steps, warmup, use_graph, step=step)
+        row[name] = {"us_per_launch": round(sec * 1e6, 2),
+                     "packed_gb_per_s": round(p.numel() / sec / 1e9, 1),
+                     "frac_of_hbm_peak": round(p.numel() / sec / 1e9 / PEAK_HBM_GBS, 4),
+                     "t_weights_per_s": round(M * K / sec / 1e12, 2)}
+    row["base3_over_2bit_weights_per_s"] = round(
+        row["b3t1024_base3"]["t_weights_per_s"] / row["t16q256_2bit"]["t_weights_per_s"], 3)
+    res["steady_state_tall_matrix"] = row
+    del tall
+    torch.cuda.empty_cache()
     return res
 
 
@@ -454,6 +480,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     bt.lib()  # fail loudly if the HIP library is missing
+
+    if args.base3_only:
+        res = base3_extra(args.steps, args.warmup, not args.no_graph, args.layers or 8)
+        print(json.dumps({"base3_vs_2bit_70b": res}), flush=True)
+        return
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
