@@ -91,3 +91,53 @@ def test_weight_quantizer_graph_replays():
         assert torch.equal(stats, ref_stats), f"replay {rep} stats"
         step()
         torch.cuda.synchronize()
+
+
+def test_base3_graph_replays():
+    # base-3 packing and decode products (every launch shape of the product:
+    # no K split on a tall matrix, a K split on a short one, four tokens)
+    # captured together; replays equal the eager results
+    shapes = [(24576, 1024), (64, 4096)]
+    mats = []
+    for i, (M, K) in enumerate(shapes):
+        w = W.ternary_weights(M, K, "p0_0.4", 40 + i, device=DEV)
+        packed = torch.empty(bt.bt_b3_bytes(M, K), dtype=torch.uint8, device=DEV)
+        outs = []
+        for N in (1, 4):
+            xq, xs, xsum = bt.quant_act(W.activations(N, K, "normal", 50 + i + N, "bf16",
+                                                      device=DEV))
+            outs.append((N, xq, xs, xsum, torch.empty((N, M), dtype=torch.bfloat16, device=DEV)))
+        mats.append((M, K, w, packed, outs))
+
+    def step():
+        for M, K, w, packed, outs in mats:
+            bt.bt_pack_ternary_b3(w, M, K, 0.02, packed)
+            for N, xq, xs, xsum, y in outs:
+                bt.bt_ternary_gemv_b3(packed, M, K, xq, xs, xsum, N, y, bt.BT_BF16)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [(m[3].clone(), [o[4].clone() for o in m[4]]) for m in mats]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for m in mats:
+            m[3].fill_(0)
+            for o in m[4]:
+                o[4].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for m, (ep, ey) in zip(mats, eager):
+            assert torch.equal(m[3], ep), f"replay {rep} packed"
+            for o, e in zip(m[4], ey):
+                assert torch.equal(o[4], e), f"replay {rep} N={o[0]}"
+        step()
+        torch.cuda.synchronize()
