@@ -55,7 +55,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps before the timed ones (the default, ~0.2 s of "
+                         "the 70B-class stream, lets the chip reach its steady clocks)")
     ap.add_argument("--workload", default="stream70b")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per step (default: the workload's first batch)")
@@ -341,9 +343,14 @@ def prefill_extra(steps, warmup, use_graph):
     wl = W.PREFILL2B_N2048
     m = Model(wl, 1, "cuda:0")
     m.set_tokens(2048)
-    # one block per step: all timed steps in one graph (a model's graph holds
-    # its 30 blocks), so one replay launch is not charged to every block
-    sec, _ = run_steps(m, steps, steps, use_graph, per_graph=steps)
+    # one block per step: 20 steps per graph (a model's graph holds its 30
+    # blocks), so one replay launch is not charged to every block.  A step is
+    # only ~0.15 ms: at least 2000 warm-up steps (~0.3 s) bring the chip to
+    # its steady clocks, and at least 200 timed steps average out the noise.
+    per_graph = 20
+    steps = max(steps, 200) // per_graph * per_graph
+    sec, _ = run_steps(m, steps, max(warmup, 2000) // per_graph * per_graph, use_graph,
+                       per_graph=per_graph)
     ops = 2 * 2048 * sum(M * K for M, K in wl.shapes)
     kt, launches = kernel_pass(m, steps)
     per_launch_ops = ops / 4
