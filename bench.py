@@ -478,7 +478,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path", file=sys.stderr)
+              "the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as W
