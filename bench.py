@@ -327,6 +327,34 @@ def cpu_baseline(wl, N, budget_s):
             break
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     cores = min(cores, len(os.sched_getaffinity(0)))
+    # the same oracle on one thread (OpenMP's thread count of this thread;
+    # the results do not depend on it), on a shorter sample
+    one = None
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            for p, (M, K) in enumerate(wl.shapes):
+                oracle.forward(packed[p], M, K, xs[wl.proj_input[p]])
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= budget_s / 4:
+                break
+        gomp.omp_set_num_threads(cores)
+        one = round(wl.packed_bytes_per_layer * reps1 / el1 / 1e9, 4)
+    except OSError:
+        pass
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(wl.packed_bytes_per_layer * reps / el / 1e9, 4),
         "unit": "GB/s",
@@ -334,6 +362,9 @@ def cpu_baseline(wl, N, budget_s):
         "kind": "oracle",
         "sample": f"layer 0 of {wl.name} (all 7 projections, {N} token(s)), "
                   f"{reps} pass(es) in {el:.1f} s",
+        "one_thread_value": one,
+        "cpu_model": cpu_model,
+        "compile_flags": " ".join(oracle.CFLAGS),
     }
 
 
@@ -397,6 +428,79 @@ def weight_quant_extra(steps, warmup):
                      "frac_of_hbm_peak": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
     del w, packed
     torch.cuda.empty_cache()
+    return res
+
+
+def small_configs_extra(steps, warmup, use_graph):
+    """The single 2560 x 2560 GEMV and the 2B-style block at 1 and 64 tokens,
+    hot (the same weights every call: they stay in the 256 MB last-level
+    cache) and cold (distinct weight copies in rotation, more than 256 MB in
+    all), per call of the whole path (quantization included)."""
+    import torch
+    import ternary_weight_quantized_bt_amd as bt
+    import workloads as W
+    dev = "cuda:0"
+    res = {}
+    # single GEMV: quantize the token, then the product
+    wl = W.GEMV_2560
+    M, K = wl.shapes[0]
+    x = W.layer_inputs(wl, 0, 1, dev)[0]
+    xq = torch.empty((1, K), dtype=torch.int8, device=dev)
+    xsc = torch.empty(1, dtype=torch.float32, device=dev)
+    xsm = torch.empty(1, dtype=torch.int32, device=dev)
+    y = torch.empty((1, M), dtype=torch.float32, device=dev)
+    row = {}
+    for name, copies in (("hot", 1), ("cold", 192)):
+        ps = [bt.pack(W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, c, 0), dev), 0.02)
+              for c in range(copies)]
+
+        def step():
+            for pk in ps:
+                bt.bt_quant_act(x, bt.BT_F32, 1, K, xq, xsc, xsm)
+                bt.bt_ternary_gemv(pk, M, K, xq, xsc, xsm, 1, y, bt.BT_F32)
+        reps = 20 if copies == 1 else 1
+        sec, _ = run_steps(None, steps * reps, warmup * reps, use_graph, step=step,
+                           per_graph=reps)
+        per = sec / copies
+        row[name] = {"copies": copies, "us_per_call": round(per * 1e6, 3),
+                     "packed_gb_per_s": round(M * K / 4 / per / 1e9, 1)}
+        del ps
+    res["gemv_2560"] = row
+    for wl, N in ((W.LAYER2B_N1, 1), (W.LAYER2B_N64, 64)):
+        row = {}
+        for name, layers in (("hot", 1), ("cold", 16)):
+            m = Model(wl, layers, dev)
+            m.set_tokens(N)
+            reps = 20 if layers == 1 else 1
+            sec, _ = run_steps(m, steps * reps, warmup * reps, use_graph, per_graph=reps)
+            per = sec / layers
+            row[name] = {"blocks": layers, "us_per_block": round(per * 1e6, 3),
+                         "packed_gb_per_s": round(wl.packed_bytes_per_layer / per / 1e9, 1),
+                         "frac_of_hbm_peak": round(wl.packed_bytes_per_layer / per / 1e9 / PEAK_HBM_GBS, 4)}
+            if N > 1:
+                ops = 2 * N * sum(M * K for M, K in wl.shapes)
+                row[name]["int8_tops"] = round(ops / per / 1e12, 1)
+            del m
+            torch.cuda.empty_cache()
+        res[wl.name] = row
+    return res
+
+
+def copy_bandwidth_extra():
+    """Device-to-device copies (torch), 1 MB to 8 GB: bytes read + written per
+    second, the measured reference beside the 8 TB/s specification."""
+    import torch
+    res = {}
+    for size in (1 << 20, 16 << 20, 256 << 20, 1 << 30, 4 << 30, 8 << 30):
+        src = torch.ones(size, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        reps = max(3, min(200, (8 << 30) // size))
+        for _ in range(3):
+            dst.copy_(src)
+        t, _ = time_region(lambda: dst.copy_(src), reps)
+        res[f"{size >> 20}MB"] = round(2 * size * reps / t / 1e9, 1)
+        del src, dst
+        torch.cuda.empty_cache()
     return res
 
 
@@ -594,6 +698,13 @@ def main():
         extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
         extra["weight_quantizer_70b_gate"] = weight_quant_extra(args.steps, args.warmup)
         extra["base3_vs_2bit_70b"] = base3_extra(args.steps, args.warmup, use_graph)
+        extra["small_configs_hot_and_cold"] = small_configs_extra(args.steps, args.warmup,
+                                                                  use_graph)
+        copy = copy_bandwidth_extra()
+        extra["device_copy_gb_per_s_read_plus_write"] = copy
+        # copies of 1 GB and more run from HBM (smaller ones from the caches)
+        hbm_copy = max(v for k, v in copy.items() if int(k[:-2]) >= 1024)
+        extra["value_over_hbm_device_copy"] = round(value / hbm_copy, 4)
 
     cpu = None
     if not args.no_cpu:
