@@ -94,7 +94,7 @@ def kernel_sha(kernel_name: str) -> str:
 class Model:
     """Packed weights of every layer plus per-step inputs, outputs, workspace."""
 
-    def __init__(self, wl, layers, device):
+    def __init__(self, wl, layers, device, base3=False):
         import torch
         import ternary_weight_quantized_bt_amd as bt
         import workloads as W
@@ -108,14 +108,16 @@ class Model:
                 w = W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, l, p), device)
                 torch.cuda.synchronize()
                 a = time.perf_counter()
-                packed.append(bt.pack(w, W.weight_scale(wl, p)))
+                packed.append(bt.pack_b3(w, W.weight_scale(wl, p)) if base3
+                              else bt.pack(w, W.weight_scale(wl, p)))
                 torch.cuda.synchronize()
                 pack_s += time.perf_counter() - a
                 del w
-            self.layer_objs.append(bt.Layer(packed, wl.shapes))
+            self.layer_objs.append(bt.Layer(packed, wl.shapes, base3=base3))
         self.setup_s = time.perf_counter() - t0
         self.pack_s = pack_s
-        self.packed_bytes = wl.packed_bytes_per_layer * layers
+        self.packed_bytes = (sum(t.numel() - 256 for t in self.layer_objs[0].packed) * layers
+                             if base3 else wl.packed_bytes_per_layer * layers)
 
     def set_tokens(self, N):
         import torch
@@ -431,6 +433,26 @@ def weight_quant_extra(steps, warmup):
     return res
 
 
+def base3_stream_extra(wl, layers, steps, warmup, use_graph, value_2bit, sec_2bit):
+    """The same 1-token stream with the weights in the base-3 B3T1024 format
+    (1.625 bits per weight): one launch per block, the base-3 decode."""
+    import torch
+    m = Model(wl, layers, "cuda:0", base3=True)
+    m.set_tokens(1)
+    sec, _ = run_steps(m, steps, warmup, use_graph)
+    weights = sum(M * K for M, K in wl.shapes) * layers
+    res = {"ms_per_step": round(sec * 1e3, 4),
+           "packed_gb": round(m.packed_bytes / 1e9, 3),
+           "packed_gb_per_s": round(m.packed_bytes / sec / 1e9, 1),
+           "frac_of_hbm_peak": round(m.packed_bytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+           "t_weights_per_s": round(weights / sec / 1e12, 2),
+           "t_weights_per_s_2bit": round(weights / sec_2bit / 1e12, 2),
+           "step_speedup_over_2bit": round(sec_2bit / sec, 3)}
+    del m
+    torch.cuda.empty_cache()
+    return res
+
+
 def small_configs_extra(steps, warmup, use_graph):
     """The single 2560 x 2560 GEMV and the 2B-style block at 1 and 64 tokens,
     hot (the same weights every call: they stay in the 256 MB last-level
@@ -698,6 +720,10 @@ def main():
         extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
         extra["weight_quantizer_70b_gate"] = weight_quant_extra(args.steps, args.warmup)
         extra["base3_vs_2bit_70b"] = base3_extra(args.steps, args.warmup, use_graph)
+        if wl.name == "stream70b" and N == 1:
+            extra["stream70b_1_token_base3"] = base3_stream_extra(wl, layers, args.steps,
+                                                                  args.warmup, use_graph,
+                                                                  value, sec)
         extra["small_configs_hot_and_cold"] = small_configs_extra(args.steps, args.warmup,
                                                                   use_graph)
         copy = copy_bandwidth_extra()

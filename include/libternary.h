@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 5
+#define BT_ABI_VERSION 6
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -346,11 +346,19 @@ typedef struct {
     bt_dtype y_dtype;                   /* BT_F32, BT_BF16 or BT_I32 */
     void *workspace;                    /* device scratch, 256-byte aligned */
     size_t workspace_bytes;             /* >= bt_layer_workspace_bytes() */
-    uint32_t flags;                     /* 0 or BT_LAYER_PER_GROUP */
+    uint32_t flags;                     /* 0, BT_LAYER_PER_GROUP, BT_LAYER_BASE3 */
 } bt_layer_io;
 
 /* io->flags: run the four groups as four launches even where one would do. */
 #define BT_LAYER_PER_GROUP 1u
+/* The seven weight pointers hold base-3 B3T1024 bytes (bt_pack_ternary_b3;
+ * every K a multiple of 1024).  Results are those of the T16Q256 path on the
+ * same weights.  1..2 tokens with every K >= 4096 and N * (sum of the four
+ * input widths) <= 80 KiB (e.g. 1 token of an 8192/28672 block) run as ONE
+ * launch, as above, with the base-3 decode; otherwise the inputs are
+ * quantized into the workspace and each projection is a bt_ternary_gemv_b3
+ * product. */
+#define BT_LAYER_BASE3 2u
 
 /* Scratch needed by bt_layer_forward for N tokens (quantized inputs, their
  * scales and sums).  Returns 0 if the layer's shapes are invalid. */
@@ -359,9 +367,9 @@ size_t bt_layer_workspace_bytes(const bt_layer *layer, int64_t N);
 bt_status bt_layer_forward(const bt_layer *layer, const bt_layer_io *io,
                            bt_stream stream);
 
-/* 1 if bt_layer_forward runs this layer for N tokens of x_dtype as one launch
- * (without BT_LAYER_PER_GROUP), 0 if as per-group launches, -1 if the layer
- * or the arguments are invalid.  Host-only; no GPU work. */
+/* 1 if bt_layer_forward runs this layer of T16Q256 weights for N tokens of
+ * x_dtype as one launch (io->flags 0), 0 if as per-group launches, -1 if the
+ * layer or the arguments are invalid.  Host-only; no GPU work. */
 int bt_layer_one_launch(const bt_layer *layer, int64_t N, bt_dtype x_dtype);
 
 #ifdef __cplusplus

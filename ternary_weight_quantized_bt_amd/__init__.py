@@ -78,12 +78,13 @@ class bt_layer_io(ctypes.Structure):
 
 
 BT_LAYER_PER_GROUP = 1
+BT_LAYER_BASE3 = 2
 BT_WSCALE_ABSMEAN = 0
 BT_WSCALE_ABSMAX = 1
 BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 
@@ -414,12 +415,14 @@ def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
 
 
 class Layer:
-    """Seven packed projections (q, k, v, o, gate, up, down) of one block."""
+    """Seven packed projections (q, k, v, o, gate, up, down) of one block
+    (T16Q256 bytes, or base-3 B3T1024 bytes with base3=True)."""
 
-    def __init__(self, packed, shapes):
+    def __init__(self, packed, shapes, base3=False):
         assert len(packed) == BT_LAYER_PROJ and len(shapes) == BT_LAYER_PROJ
         self.packed = list(packed)  # keeps the tensors alive
         self.shapes = [tuple(s) for s in shapes]
+        self.base3 = base3
         self.c = bt_layer()
         for p, (t, (M, K)) in enumerate(zip(self.packed, self.shapes)):
             self.c.w[p] = _p(t)
@@ -431,7 +434,7 @@ class Layer:
 
     def make_io(self, xs, ys, y_dtype, workspace, per_group=False) -> bt_layer_io:
         io = bt_layer_io()
-        io.flags = BT_LAYER_PER_GROUP if per_group else 0
+        io.flags = (BT_LAYER_PER_GROUP if per_group else 0) | (BT_LAYER_BASE3 if self.base3 else 0)
         io.N = xs[0].shape[0]
         for i, x in enumerate(xs):
             io.x[i] = _p(x)

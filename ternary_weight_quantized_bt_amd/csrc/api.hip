@@ -381,8 +381,9 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
     int64_t Kin[BT_LAYER_INPUTS];
     if (!layer_input_widths(L, Kin))
         return fail(BT_ERR_SHAPE, "%s: q/k/v (or gate/up) have different K", fn);
+    const bool base3 = (io->flags & BT_LAYER_BASE3) != 0;
     for (int p = 0; p < BT_LAYER_PROJ; ++p) {
-        BT_TRY(check_mk(L->M[p], L->K[p], fn));
+        BT_TRY(base3 ? check_b3(L->M[p], L->K[p], fn) : check_mk(L->M[p], L->K[p], fn));
         BT_TRY(check_ptr(L->w[p], "layer->w[p]", fn));
     }
     const int64_t N = io->N;
@@ -391,7 +392,7 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         return fail(BT_ERR_DTYPE, "%s: x dtype must be BT_F32 or BT_BF16", fn);
     if (io->y_dtype != BT_F32 && io->y_dtype != BT_BF16 && io->y_dtype != BT_I32)
         return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)io->y_dtype);
-    if (io->flags & ~BT_LAYER_PER_GROUP)
+    if (io->flags & ~(BT_LAYER_PER_GROUP | BT_LAYER_BASE3))
         return fail(BT_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, (unsigned)io->flags);
     if (N == 0) return ok();
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) BT_TRY(check_ptr(io->x[i], "io->x[i]", fn));
@@ -404,6 +405,43 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         return fail(BT_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
 
     hipStream_t s = as_stream(stream);
+    if (base3) {
+        const bool per_group = (io->flags & BT_LAYER_PER_GROUP) != 0;
+        if (!per_group && bt::layer_fusable(Kin, L->M, N, io->x_dtype, true)) {
+            const bt::LayerArgs la =
+                bt::make_layer_args(L->w, L->M, Kin, io->x, io->y, N, io->y_dtype, true);
+            const hipError_t e = bt::launch_layer(la, io->x_dtype, s);
+            return e == hipSuccess ? ok() : hip_status(e, fn);
+        }
+        // the inputs quantized into the workspace (one launch, or one per
+        // group before its products), then one base-3 product per projection
+        const LayerWs ws = carve(Kin, N, io->workspace);
+        if (!per_group) {
+            bt::QuantJobs jobs{};
+            for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+                jobs.x[i] = io->x[i];
+                jobs.K[i] = Kin[i];
+                jobs.xq[i] = ws.xq[i];
+                jobs.xs[i] = ws.xs[i];
+                jobs.xsum[i] = ws.xsum[i];
+            }
+            const hipError_t e = bt::launch_quant_jobs(jobs, BT_LAYER_INPUTS, io->x_dtype, N, s);
+            if (e != hipSuccess) return hip_status(e, fn);
+        }
+        static const int kGroupOf[BT_LAYER_PROJ] = {0, 0, 0, 1, 2, 2, 3};
+        for (int p = 0; p < BT_LAYER_PROJ; ++p) {
+            const int i = kGroupOf[p];
+            hipError_t e = hipSuccess;
+            if (per_group && (p == 0 || kGroupOf[p - 1] != i))
+                e = bt::launch_quant(io->x[i], io->x_dtype, N, Kin[i], ws.xq[i], ws.xs[i],
+                                     ws.xsum[i], s);
+            if (e == hipSuccess)
+                e = bt::launch_b3_gemv(L->w[p], L->M[p], Kin[i], ws.xq[i], ws.xs[i], ws.xsum[i],
+                                       N, io->y[p], io->y_dtype, s);
+            if (e != hipSuccess) return hip_status(e, fn);
+        }
+        return ok();
+    }
     if (!(io->flags & BT_LAYER_PER_GROUP) && N < BT_PREFILL_MIN_N &&
         bt::layer_fusable(Kin, L->M, N, io->x_dtype)) {
         // one launch for the whole block

@@ -16,33 +16,16 @@
 //   b; words 0..11 sit in three 16-byte chunks at 16 (64 i + l) (a wave reads
 //   each chunk row with one coalesced 128-bit load), word 12 at 3072 + 4 l.
 //
-// GPU decode.  A byte's four low base-3 digits are the codes of four
-// consecutive columns -- one int8x4 dot operand -- and its fifth digit is the
-// code of one of columns 48..59.  Rather than divide, every workgroup builds a
-// table in LDS: entry v holds the four low digits of v as bytes and, in a
-// second word, the fifth digit v / 81 repeated in all four bytes.  One 8-byte
-// LDS read per weight byte yields a dot operand ready to use, and the fifth
-// digits of four bytes are merged into the operand of columns 48+4g..51+4g
-// with two byte permutes and an or.  The table is stored 32 times over (lane l
-// reads copy l % 32 at byte v * 256 + 8 (l % 32)), so any 32 lanes served
-// together hit 32 distinct 8-byte bank pairs whatever the weights are: table
-// lookups without bank conflicts.  Per 64 weights a lane spends 13 byte
-// permutes (the table address of each byte), 13 LDS reads, 9 merge operations
-// and 16 dot4 per token (the 2-bit decode: 20 bit operations and 16 dot4).
+// The decode (an LDS table of the four low digits of every byte value, the
+// fifth digits merged with byte permutes) is in base3.hpp, shared with the
+// per-layer kernel.
 
-#include "common.hpp"
+#include "base3.hpp"
 #include "internal.hpp"
 
 namespace bt {
 
 namespace {
-
-constexpr int kB3Cols = 1024;        // columns of one B3 tile
-constexpr int kB3TileBytes = 3328;   // 16 x 1024 codes at 1.625 bits
-constexpr int kB3Copies = 32;        // table copies (lane % 32)
-constexpr int kB3TabBytes = 256 * kB3Copies * 8;  // every byte value, 8 bytes per entry
-
-__device__ __forceinline__ int64_t b3_code_bytes(int64_t M, int64_t K) { return M * K / 64 * 13; }
 
 // ---------------------------------------------------------------- packing --
 
@@ -118,11 +101,6 @@ void b3_pack_kernel(const int8_t *__restrict__ w, int64_t M, int64_t K, float sc
     }
 }
 
-// The four low base-3 digits of a byte as four bytes (codes, 0..2).
-__device__ __forceinline__ uint32_t low_digits(uint32_t v) {
-    return (v % 3) | ((v / 3 % 3) << 8) | ((v / 9 % 3) << 16) | ((v / 27 % 3) << 24);
-}
-
 // Inverse of b3_pack_kernel: w = code - 1.
 __global__ __launch_bounds__(kB3PackThreads)
 void b3_unpack_kernel(const uint8_t *__restrict__ packed, int64_t M, int64_t K,
@@ -188,73 +166,6 @@ struct B3Args {
     int ydt;
 };
 
-// One lane's share of one tile: 13 words.
-struct B3Slot {
-    v4u c0, c1, c2;
-    uint32_t last;
-};
-
-__device__ __forceinline__ B3Slot load_slot(const uint8_t *tile, int lane) {
-    const gptr<const v4u> p = to_global(reinterpret_cast<const v4u *>(tile)) + lane;
-    B3Slot s;
-    s.c0 = p[0];
-    s.c1 = p[64];
-    s.c2 = p[128];
-    s.last = to_global(reinterpret_cast<const uint32_t *>(tile + 3072))[lane];
-    return s;
-}
-
-// Table entry of byte i of `word` for this lane: {low digits, fifth digit x 4}.
-// v_perm_b32 builds the LDS byte address v * 256 + l8 in one instruction:
-// result byte 0 = byte 0 of l8, result byte 1 = byte i of word, bytes 2, 3 = 0.
-__device__ __forceinline__ uint2 lookup(const uint8_t *tab, uint32_t word, int i, uint32_t l8) {
-    const uint32_t addr = __builtin_amdgcn_perm(word, l8, 0x0C0C0000u | ((4u + i) << 8));
-    return *reinterpret_cast<const uint2 *>(tab + addr);
-}
-
-// Byte i of the result from byte 0 of hi (each hi holds one value in all
-// four bytes): two byte permutes and an or.
-__device__ __forceinline__ uint32_t merge4(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3) {
-    const uint32_t lo = __builtin_amdgcn_perm(h1, h0, 0x0C0C0400u);  // h0 h1 0 0
-    const uint32_t hi = __builtin_amdgcn_perm(h3, h2, 0x04000C0Cu);  // 0 0 h2 h3
-    return lo | hi;
-}
-
-// Adds sum_k code[k] * x[n, k] over the lane's 256 columns of one tile for
-// tokens n < nvalid.  x points at the lane's first column of token 0; token
-// rows are K bytes apart.
-template <int NT>
-__device__ __forceinline__ void b3_dot(const B3Slot &sl, const uint8_t *tab, uint32_t l8,
-                                       const int8_t *x, int64_t K, int nvalid, int acc[NT]) {
-    const uint32_t w[13] = {sl.c0.x, sl.c0.y, sl.c0.z, sl.c0.w, sl.c1.x, sl.c1.y, sl.c1.z,
-                            sl.c1.w, sl.c2.x, sl.c2.y, sl.c2.z, sl.c2.w, sl.last};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        uint2 e[12];
-#pragma unroll
-        for (int j = 0; j < 12; ++j) e[j] = lookup(tab, w[3 * b + j / 4], j % 4, l8);
-        const uint32_t e12 = lookup(tab, w[12], b, l8).x;
-        uint32_t d[3];
-#pragma unroll
-        for (int g = 0; g < 3; ++g)
-            d[g] = merge4(e[4 * g].y, e[4 * g + 1].y, e[4 * g + 2].y, e[4 * g + 3].y);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            if (n >= nvalid) break;
-            const uint4 *xv = reinterpret_cast<const uint4 *>(x + n * K + 64 * b);
-            const uint4 a0 = xv[0], a1 = xv[1], a2 = xv[2], a3 = xv[3];
-            const uint32_t xa[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                     a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-            int s = acc[n];
-#pragma unroll
-            for (int j = 0; j < 12; ++j) s = __builtin_amdgcn_sdot4((int)e[j].x, (int)xa[j], s, false);
-#pragma unroll
-            for (int g = 0; g < 3; ++g) s = __builtin_amdgcn_sdot4((int)d[g], (int)xa[12 + g], s, false);
-            acc[n] = __builtin_amdgcn_sdot4((int)e12, (int)xa[15], s, false);
-        }
-    }
-}
-
 // Decode product over B3 tiles.  Persistent grid: each workgroup builds the
 // table and stages the activations (LDSX) in LDS, then walks the 16-row
 // tiles with a stride of the grid.  Its WAVES waves split K into P contiguous
@@ -315,17 +226,8 @@ void b3_gemv_kernel(B3Args a) {
     }
 
     // ---- prologue: the table, the activations, the per-token constants ----
-    // Thread t computes entry v = t / 4 once and writes copies 8 (t % 4) ..
-    // 8 (t % 4) + 7: 64 contiguous bytes at v * 256 + 64 (t % 4).
     uint8_t *tab = b3_smem;
-    for (int t = threadIdx.x; t < 256 * 4; t += kThreads) {
-        const uint32_t v = (uint32_t)t / 4;
-        const uint32_t lo = v < 243 ? low_digits(v) : 0u;
-        const uint32_t hi = v < 243 ? (v / 81) * 0x01010101u : 0u;
-        v4u *dst = reinterpret_cast<v4u *>(tab + 64 * t);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[c] = v4u{lo, hi, lo, hi};
-    }
+    b3_build_table(tab, (int)threadIdx.x, kThreads);
     const int8_t *xsrc = a.xq;
     if (LDSX) {
         int8_t *xl = reinterpret_cast<int8_t *>(b3_smem + kB3TabBytes);

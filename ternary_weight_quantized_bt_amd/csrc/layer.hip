@@ -42,7 +42,9 @@
 // per tile), and the epilogue dequantizes.
 
 #include <algorithm>
+#include <type_traits>
 
+#include "base3.hpp"
 #include "dot4.hpp"
 #include "layer.hpp"
 #include "quant.hpp"
@@ -55,6 +57,15 @@ constexpr int kLayerWaves = 16;
 constexpr int kLayerThreads = kLayerWaves * kWave;
 constexpr int kLayerSplit = 8;  // K split over 8 waves: two tiles per iteration
 constexpr int kLayerRing = 4;
+constexpr int kLayerRingB3 = 2;  // base-3 slots are 13 words
+// K split of base-3 tiles (1024-column tile columns): 4 measured fastest on the
+// 70B-class stream (8 / 4 / 2 / 1: 3.71 / 3.60 / 3.84 / 5.45 ms per 80 blocks;
+// a third ring slot costs 3-4 %).
+constexpr int kLayerSplitB3 = 4;
+// Codes of all four inputs beside the 64 KiB base-3 table.
+constexpr int64_t kLayerLdsMaxB3 = 80 * 1024;
+// An iteration's fixed cost in base-3 tile columns (8 KiB of streaming).
+constexpr int kIterCostB3 = 2;
 constexpr int kLayerUnits = 8;  // input chunks held per lane
 constexpr int64_t kLayerLdsMax = 128 * 1024;  // token codes of all four inputs
 constexpr int64_t kLayerMinK = (int64_t)kTileCols * kLayerSplit;  // a block per wave
@@ -100,7 +111,9 @@ struct Chunk<uint16_t> {
         return e;
     }
 };
-template <typename T, int NT, int WAVES, int P, int RING>
+// B3: the weights are base-3 B3T1024 tiles (16 rows x 1024 columns, base3.hpp)
+// instead of T16Q256 ones; a K split part is then a 1024-column tile column.
+template <typename T, int NT, int WAVES, int P, int RING, bool B3>
 __global__ __launch_bounds__(WAVES * kWave)
 void layer_dot4_kernel(LayerArgs a) {
     static_assert(WAVES % P == 0, "K split must divide the waves");
@@ -256,8 +269,9 @@ void layer_dot4_kernel(LayerArgs a) {
     }
     // Weight scale of projection min(wave, 6) (from its packed tail).
     const int wp = min(wave, kLayerProj - 1);
-    const float ws = *to_global(reinterpret_cast<const float *>(
-        sel(a.packed, wp) + sel(a.M, wp) * sel(a.K, proj_group(wp)) / 4));
+    const int64_t code_bytes = B3 ? b3_code_bytes(sel(a.M, wp), sel(a.K, proj_group(wp)))
+                                  : sel(a.M, wp) * sel(a.K, proj_group(wp)) / 4;
+    const float ws = *to_global(reinterpret_cast<const float *>(sel(a.packed, wp) + code_bytes));
     if (threadIdx.x < kKeys) {
         s_amax[threadIdx.x] = 0;
         s_sum[threadIdx.x] = 0;
@@ -267,7 +281,8 @@ void layer_dot4_kernel(LayerArgs a) {
     // current one included), lleft slots left to load.  On the last slot it
     // stays put, so every ring load is unconditional (a harmless reload).
     int lit = 0, lrem = 0, lleft = nslots;
-    gptr<const v4u> lp;
+    gptr<const v4u> lp;        // T16Q256: this lane's 16 bytes of the slot
+    const uint8_t *lt = nullptr;  // B3T1024: the tile
     Win lw = win0();
     int lnq = 0, lqb = 0;
     const uint8_t *lbase = nullptr;
@@ -280,26 +295,42 @@ void layer_dot4_kernel(LayerArgs a) {
             lbase = sel(a.packed, lw.p);
         }
         lrem = lnq;
-        lp = to_global(reinterpret_cast<const v4u *>(
-                 lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kTileBytes)) + lane;
+        if constexpr (B3)
+            lt = lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kB3TileBytes;
+        else
+            lp = to_global(reinterpret_cast<const v4u *>(
+                     lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kTileBytes)) + lane;
     };
     point(has_work ? tile_of(0) : 0);
     auto advance_load = [&]() {
         if (lleft <= 1) return;
         --lleft;
         if (--lrem > 0) {
-            lp += kWave * P;
+            if constexpr (B3)
+                lt += (int64_t)kB3TileBytes * P;
+            else
+                lp += kWave * P;
             return;
         }
         point(tile_of(++lit));
     };
+    using Slot = typename std::conditional<B3, B3Slot, v4u>::type;
+    auto load = [&]() -> Slot {
+        if constexpr (B3)
+            return load_slot<true>(lt, lane);
+        else
+            return __builtin_nontemporal_load(lp);
+    };
     constexpr int kSlots = RING + 1;
-    v4u ring[kSlots];
+    Slot ring[kSlots];
 #pragma unroll
     for (int d = 0; d < RING; ++d) {
-        ring[d] = __builtin_nontemporal_load(lp);
+        ring[d] = load();
         advance_load();
     }
+    if constexpr (B3)
+        b3_build_table(reinterpret_cast<uint8_t *>(codes) + a.tab32, (int)threadIdx.x,
+                       (int)(WAVES * kWave));
     __syncthreads();  // zeroed tables
 
     // ---- prologue, part 2: absmax per (group, token) ----
@@ -396,7 +427,7 @@ void layer_dot4_kernel(LayerArgs a) {
             const int g = proj_group(cw.p);
             cnq = nq(g);
             cK = sel(a.k32, g);
-            xb = codes + sel(a.xoff32, g) + 16 * h;
+            xb = codes + sel(a.xoff32, g) + (B3 ? 256 : 16) * h;
             cfirst = false;
         }
         cq = kpart;
@@ -408,11 +439,21 @@ void layer_dot4_kernel(LayerArgs a) {
     Win ow = win0();  // the tiles this wave stores (waves < TPW)
     Acc<NT> acc;
     acc_zero(acc);
+    int iacc[NT];  // B3 sums
+#pragma unroll
+    for (int j = 0; j < NT; ++j) iacc[j] = 0;
+    const uint8_t *tab = reinterpret_cast<const uint8_t *>(codes) + a.tab32;
+    const uint32_t l8 = 8u * (uint32_t)(lane % kB3Copies);
     auto iter_done = [&](int it) {
         int v[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            v[j] = acc_total(acc, j);
+            if constexpr (B3) {
+                v[j] = iacc[j];
+                iacc[j] = 0;
+            } else {
+                v[j] = acc_total(acc, j);
+            }
             v[j] += __shfl_xor(v[j], 16, kWave);
             v[j] += __shfl_xor(v[j], 32, kWave);
         }
@@ -453,8 +494,13 @@ void layer_dot4_kernel(LayerArgs a) {
 #pragma unroll
         for (int d = 0; d < kSlots; ++d) {
             const int i = base + d;
-            if (i < nslots) dot_slot<NT>(ring[d], xb + cq * kTileCols, cK, nvalid, acc);
-            ring[(d + RING) % kSlots] = __builtin_nontemporal_load(lp);
+            if (i < nslots) {
+                if constexpr (B3)
+                    b3_dot<NT>(ring[d], tab, l8, xb + cq * kB3Cols, cK, nvalid, iacc);
+                else
+                    dot_slot<NT>(ring[d], xb + cq * kTileCols, cK, nvalid, acc);
+            }
+            ring[(d + RING) % kSlots] = load();
             advance_load();
             if (i < nslots) {
                 cq += P;
@@ -484,8 +530,10 @@ void layer_dot4_kernel(LayerArgs a) {
 // block: 0, 8, 32 and 64 give 1.3 %, 1.9 %, -5 % and -0.8 % against striding.
 constexpr int kIterCostBlocks = 8;
 
+// iter_cost: the same fixed cost in the schedule's units (256-column blocks,
+// or 1024-column base-3 tile columns: 3.25 KiB each).
 template <int TPW>
-void plan_schedule(LayerArgs &a, int G) {
+void plan_schedule(LayerArgs &a, int G, int iter_cost) {
     a.sched = 0;
     const int total = a.tend32[kLayerProj - 1];
     const int T = (total + TPW - 1) / TPW;
@@ -497,7 +545,7 @@ void plan_schedule(LayerArgs &a, int G) {
         return a.qb32[g];
     };
     auto group_cost = [&](int tg) {
-        int c = kIterCostBlocks;
+        int c = iter_cost;
         for (int k = 0; k < TPW; ++k) c += tile_cost(tg * TPW + k);
         return c;
     };
@@ -563,20 +611,21 @@ void plan_schedule(LayerArgs &a, int G) {
     }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, bool B3>
 hipError_t launch_layer_t(const LayerArgs &args, size_t lds, hipStream_t s) {
-    auto kern = layer_dot4_kernel<T, NT, kLayerWaves, kLayerSplit, kLayerRing>;
+    constexpr int P = B3 ? kLayerSplitB3 : kLayerSplit;
+    auto kern = layer_dot4_kernel<T, NT, kLayerWaves, P, B3 ? kLayerRingB3 : kLayerRing, B3>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    constexpr int TPW = kLayerWaves / kLayerSplit;
+    constexpr int TPW = kLayerWaves / P;
     const int64_t groups = (args.tend[kLayerProj - 1] + TPW - 1) / TPW;
     const int64_t grid = min(groups, (int64_t)device_cus());
     LayerArgs a = args;
-    plan_schedule<TPW>(a, (int)grid);
+    plan_schedule<TPW>(a, (int)grid, B3 ? kIterCostB3 : kIterCostBlocks);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kLayerThreads), lds, s, a);
     return hipGetLastError();
 }
@@ -584,26 +633,27 @@ hipError_t launch_layer_t(const LayerArgs &args, size_t lds, hipStream_t s) {
 }  // namespace
 
 bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
-                   bt_dtype xdt) {
+                   bt_dtype xdt, bool b3) {
     if (N < 1 || N > 4) return false;
     if (xdt != BT_BF16) return false;  // f32 chunks would need twice the registers
     int64_t sumk = 0;
     for (int g = 0; g < kLayerInputs; ++g) {
         if (K[g] < kLayerMinK) return false;
+        if (b3 && (K[g] % kB3Cols != 0 || K[g] < (int64_t)kB3Cols * kLayerSplitB3)) return false;
         sumk += K[g];
     }
     int64_t tiles = 0;
     for (int p = 0; p < kLayerProj; ++p) tiles += M[p] / kTileRows;
     if (tiles >= (int64_t)1 << 30) return false;  // tile bookkeeping is 32-bit
     const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
-    if (nt * sumk > kLayerLdsMax) return false;
+    if (nt * sumk > (b3 ? kLayerLdsMaxB3 : kLayerLdsMax)) return false;
     const int64_t units = N * sumk / 8;
     return units <= (int64_t)kLayerUnits * kLayerThreads;
 }
 
 LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kLayerProj],
                           const int64_t K[kLayerInputs], const void *const x[kLayerInputs],
-                          void *const y[kLayerProj], int64_t N, bt_dtype ydt) {
+                          void *const y[kLayerProj], int64_t N, bt_dtype ydt, bool b3) {
     LayerArgs a{};
     int64_t end = 0;
     for (int p = 0; p < kLayerProj; ++p) {
@@ -634,19 +684,27 @@ LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kL
         a.gend32[g] = (int)a.gend[g];
         a.k32[g] = (int)a.K[g];
         a.xoff32[g] = (int)a.xoff[g];
-        a.qb32[g] = (int)(a.K[g] / kTileCols);
+        a.qb32[g] = (int)(a.K[g] / (b3 ? kB3Cols : kTileCols));
     }
     a.N = N;
     a.ydt = (int)ydt;
+    a.b3 = b3 ? 1 : 0;
+    a.tab32 = (int)((xo + 15) / 16 * 16);  // base-3 table after the codes
     return a;
 }
 
 hipError_t launch_layer(const LayerArgs &a, bt_dtype xdt, hipStream_t s) {
-    const size_t lds = (size_t)a.xoff[kLayerInputs];
     if (xdt != BT_BF16) return hipErrorInvalidValue;  // excluded by layer_fusable
-    if (a.N == 1) return launch_layer_t<uint16_t, 1>(a, lds, s);
-    if (a.N == 2) return launch_layer_t<uint16_t, 2>(a, lds, s);
-    return launch_layer_t<uint16_t, 4>(a, lds, s);
+    if (a.b3) {
+        const size_t lds = (size_t)a.tab32 + kB3TabBytes;
+        if (a.N == 1) return launch_layer_t<uint16_t, 1, true>(a, lds, s);
+        if (a.N == 2) return launch_layer_t<uint16_t, 2, true>(a, lds, s);
+        return launch_layer_t<uint16_t, 4, true>(a, lds, s);
+    }
+    const size_t lds = (size_t)a.xoff[kLayerInputs];
+    if (a.N == 1) return launch_layer_t<uint16_t, 1, false>(a, lds, s);
+    if (a.N == 2) return launch_layer_t<uint16_t, 2, false>(a, lds, s);
+    return launch_layer_t<uint16_t, 4, false>(a, lds, s);
 }
 
 }  // namespace bt

@@ -38,16 +38,21 @@ struct LayerArgs {
     // ts + n0 * heavy[0]).
     int sched, n0, ts;
     int heavy[2], sstart[2], scount[2];
+    // Weight format: 0 = T16Q256; 1 = base-3 B3T1024 (qb32 then counts
+    // 1024-column tile columns, and the decode table sits at LDS byte tab32).
+    int b3, tab32;
 };
 
 // Whether one launch can run the block: 1..4 tokens, every K at least one
 // 256-column block per wave, all token codes in LDS and all input chunks in
 // registers.
+// (b3: base-3 weights, every K a multiple of 1024 and at least one tile column
+// per wave of a K split, the codes within 80 KiB beside the decode table.)
 bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
-                   bt_dtype xdt);
+                   bt_dtype xdt, bool b3 = false);
 LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kLayerProj],
                           const int64_t K[kLayerInputs], const void *const x[kLayerInputs],
-                          void *const y[kLayerProj], int64_t N, bt_dtype ydt);
+                          void *const y[kLayerProj], int64_t N, bt_dtype ydt, bool b3 = false);
 hipError_t launch_layer(const LayerArgs &a, bt_dtype xdt, hipStream_t s);
 
 }  // namespace bt

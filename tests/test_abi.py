@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 5
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 6
 
 
 def test_packed_bytes():
@@ -246,10 +246,15 @@ def test_layer_validation():
         bt.bt_layer_forward(L, io, stream=0)
     assert e.value.status == bt.BT_ERR_INVALID_ARG
     io.y[6] = A
-    io.flags = 2  # not a defined flag
+    io.flags = 4  # not a defined flag
     with pytest.raises(bt.BtError) as e:
         bt.bt_layer_forward(L, io, stream=0)
     assert e.value.status == bt.BT_ERR_INVALID_ARG
+    io.flags = bt.BT_LAYER_BASE3  # base-3 weights need K % 1024 == 0
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_SHAPE
+    assert "1024" in bt.bt_last_error()
     io.flags = bt.BT_LAYER_PER_GROUP
     io.N = 0  # nothing to do
     bt.bt_layer_forward(L, io, stream=0)

@@ -138,3 +138,89 @@ def test_quantize_all_inputs_at_once_equals_per_group(N):
         b = L.forward(xs, y_dtype=ydt, per_group=True)
         for p in range(7):
             assert torch.equal(a[p], b[p]), (N, ydt, p)
+
+
+# ------------------------------------------------- base-3 weights ----------
+
+# every K >= 4096 and a multiple of 1024: one launch at 1 and 2 tokens (the
+# codes of two tokens fill the 80 KiB next to the decode table exactly),
+# quantization + one base-3 product per projection from 3 tokens on
+B3_BLOCK = W.Workload(
+    name="b3_block", index=9, description="block for the base-3 layer path",
+    shapes=((64, 8192), (16, 8192), (16, 8192), (48, 8192), (80, 8192),
+            (80, 8192), (32, 16384)),
+    layers=1, batches=(1, 2, 3, 5), x_dtype="bf16", y_dtype="bf16",
+    weight_dist="p0_0.4", act_dist="normal", outlier_frac=0.005, outlier_scale=30.0)
+
+
+def run_layer_b3(wl, layer, N, ydt, rows_per_proj=None, seed_rows=0, per_group=False):
+    """The driver on base-3 weights against the oracle's product."""
+    ws = W.layer_weights(wl, layer, device="cpu" if wl.layers == 1 else DEV)
+    packed = [bt.pack_b3(w.to(DEV), s) for (w, s) in ws]
+    L = bt.Layer(packed, wl.shapes, base3=True)
+    xs = W.layer_inputs(wl, layer, N, device="cpu")
+    ys = L.forward([x.to(DEV) for x in xs], y_dtype=ydt, per_group=per_group)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed_rows)
+    quant = [oracle.quant_act(x_for_oracle(x)) for x in xs]
+    for p, ((w, s), (M, K)) in enumerate(zip(ws, wl.shapes)):
+        ref_packed, _ = oracle.pack(w.cpu().numpy(), s)
+        xq, xsc, _ = quant[wl.proj_input[p]]
+        rows = None
+        if rows_per_proj is not None and rows_per_proj < M:
+            rows = np.sort(rng.choice(M, rows_per_proj, replace=False))
+        acc = oracle.matmul_i32(ref_packed, M, K, xq, rows)
+        check_projection(packed[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt,
+                         rows, f"base-3 {wl.name} layer {layer} {wl.proj_names[p]} N={N}")
+    return ys
+
+
+@pytest.mark.parametrize("N", B3_BLOCK.batches)
+@pytest.mark.parametrize("ydt", [bt.BT_I32, bt.BT_F32, bt.BT_BF16])
+def test_base3_layer(N, ydt):
+    print(f"base-3 layer N={N} ydt={ydt}", flush=True)
+    run_layer_b3(B3_BLOCK, 0, N, ydt)
+
+
+@pytest.mark.parametrize("N", [1, 3])
+def test_base3_layer_per_group(N):
+    run_layer_b3(B3_BLOCK, 0, N, bt.BT_I32, per_group=True)
+
+
+def test_base3_layer_shortest_one_launch_rows():
+    # K = 4096 everywhere: one tile column per wave of the K split
+    wl = W.Workload(**{**B3_BLOCK.__dict__, "name": "b3_4096",
+                       "shapes": ((64, 4096), (16, 4096), (16, 4096), (48, 4096),
+                                  (80, 4096), (80, 4096), (32, 4096))})
+    for N in (1, 2):
+        run_layer_b3(wl, 0, N, bt.BT_BF16)
+
+
+def test_base3_layer_short_rows():
+    # K = 1024..3072: never one launch; quantization + base-3 products
+    wl = W.Workload(**{**B3_BLOCK.__dict__, "name": "b3_short",
+                       "shapes": ((64, 2048), (16, 2048), (16, 2048), (48, 1024),
+                                  (80, 2048), (80, 2048), (32, 3072))})
+    for N in (1, 4, 9):
+        run_layer_b3(wl, 0, N, bt.BT_I32)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5])
+def test_base3_layer_equals_two_bit_layer(N):
+    # same weights in both formats: identical bf16 outputs, bit for bit
+    wl = B3_BLOCK
+    ws = W.layer_weights(wl, 0)
+    L2 = bt.Layer([bt.pack(w.to(DEV), s) for (w, s) in ws], wl.shapes)
+    L3 = bt.Layer([bt.pack_b3(w.to(DEV), s) for (w, s) in ws], wl.shapes, base3=True)
+    xs = [x.to(DEV) for x in W.layer_inputs(wl, 0, N)]
+    a = L2.forward(xs, y_dtype=bt.BT_BF16)
+    b = L3.forward(xs, y_dtype=bt.BT_BF16)
+    for p in range(7):
+        assert torch.equal(a[p], b[p]), (N, p)
+
+
+@pytest.mark.parametrize("layer", [0, 79])
+def test_workload_stream70b_base3_sampled_rows(layer):
+    # the 70B-class block in base-3 bytes at one token: one launch
+    print(f"base-3 70B-class block, layer {layer}", flush=True)
+    run_layer_b3(W.STREAM70B, layer, 1, bt.BT_BF16, rows_per_proj=64, seed_rows=layer)
