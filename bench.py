@@ -41,8 +41,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources of each measured kernel: a traffic record is only used while they
 # are unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "layer_dot4_kernel": ("layer.hip", "layer.hpp", "dot4.hpp", "common.hpp", "quant.hpp",
-                          "internal.hpp"),
+    "layer_dot4_kernel": ("layer.hip", "layer.hpp", "dot4.hpp", "base3.hpp", "common.hpp",
+                          "quant.hpp", "internal.hpp"),
     "decode_dot4_kernel (fused quantization)": ("gemv.hip", "dot4.hpp", "common.hpp", "group.hpp",
                                                 "quant.hpp"),
     "decode_dot4_kernel": ("gemv.hip", "dot4.hpp", "common.hpp", "group.hpp", "quant.hpp"),
