@@ -56,7 +56,9 @@ namespace {
 constexpr int kLayerWaves = 16;
 constexpr int kLayerThreads = kLayerWaves * kWave;
 constexpr int kLayerSplit = 8;  // K split over 8 waves: two tiles per iteration
-constexpr int kLayerRing = 4;
+// Slot loads in flight per wave: 3 measured fastest on the 70B-class stream
+// (2 / 3 / 4 / 5 / 6: 3.34 / 3.23 / 3.31 / 3.31 / 3.33 ms per 80 blocks).
+constexpr int kLayerRing = 3;
 constexpr int kLayerRingB3 = 2;  // base-3 slots are 13 words
 // K split of base-3 tiles (1024-column tile columns): 4 measured fastest on the
 // 70B-class stream (8 / 4 / 2 / 1: 3.71 / 3.60 / 3.84 / 5.45 ms per 80 blocks;
