@@ -170,9 +170,10 @@ struct B3Args {
 // table and stages the activations (LDSX) in LDS, then walks the 16-row
 // tiles with a stride of the grid.  Its WAVES waves split K into P contiguous
 // runs of 1024-column tiles (TPW = WAVES / P row tiles per iteration); each
-// wave keeps RING tile slots in flight, across tile boundaries.  Row sums are
-// reduced over the four lanes of a row (xor shuffles), then over the P waves
-// through LDS (one barrier per iteration), and dequantized.
+// wave keeps RING tile slots in flight (non-temporal loads), across tile
+// boundaries.  Row sums are reduced over the four lanes of a row (xor
+// shuffles), then over the P waves through LDS (one barrier per iteration),
+// and dequantized.
 template <int NT, bool LDSX, int WAVES, int P, int RING>
 __global__ __launch_bounds__(WAVES * kWave)
 void b3_gemv_kernel(B3Args a) {
@@ -220,7 +221,7 @@ void b3_gemv_kernel(B3Args a) {
     if (has_work) {
 #pragma unroll
         for (int d = 0; d < RING; ++d) {
-            ring[d] = load_slot(lp, lane);
+            ring[d] = load_slot<true>(lp, lane);
             advance_load();
         }
     }
@@ -301,7 +302,7 @@ void b3_gemv_kernel(B3Args a) {
         for (int d = 0; d < RING; ++d) {
             const int64_t i = base + d;
             const B3Slot cur = ring[d];
-            ring[d] = load_slot(lp, lane);
+            ring[d] = load_slot<true>(lp, lane);
             advance_load();
             if (i < nslots) {
                 b3_dot<NT>(cur, tab, l8, xb + cc * kB3Cols, K, nvalid, acc);

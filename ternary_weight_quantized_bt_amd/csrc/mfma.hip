@@ -27,8 +27,8 @@
 // once, global -> LDS with direct 16-byte loads, and then walks the 16-row
 // tiles of the group with a stride of the grid size; within a tile its waves
 // split K into contiguous runs of 256-column blocks, and each wave keeps RING
-// weight-slot loads in flight, running straight across tile boundaries (the
-// same ring as the single-token kernel).  In LDS, 16-byte chunk c of token n
+// non-temporal weight-slot loads in flight, running straight across tile
+// boundaries (the same ring as the single-token kernel).  In LDS, 16-byte chunk c of token n
 // sits at position c ^ (n % 16) of its 256-column block, so the 16 tokens an
 // instruction reads fall on 16 different bank groups.  Rows too long for LDS
 // are done in K phases: the codes of one K range at a time, all of the
@@ -194,7 +194,7 @@ __device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph,
         v4u ring[kSlots];
 #pragma unroll
         for (int d = 0; d < RING; ++d) {
-            ring[d] = *lp;
+            ring[d] = __builtin_nontemporal_load(lp);
             advance_load();
         }
         // Everything but the ring is complete and visible after this.
@@ -259,7 +259,7 @@ __device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph,
                         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_a(words[t]), B, acc, 0, 0, 0);
                     }
                 }
-                ring[(d + RING) % kSlots] = *lp;
+                ring[(d + RING) % kSlots] = __builtin_nontemporal_load(lp);
                 advance_load();
                 if (i < nslots && ++cq == q1) {
                     iter_done(cit);
