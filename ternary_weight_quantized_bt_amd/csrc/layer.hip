@@ -130,6 +130,22 @@ void layer_dot4_kernel(LayerArgs a) {
     __shared__ uint32_t s_sum[kKeys];   // code sum per (group, token)
     __shared__ float s_ws[kLayerProj];  // weight scales
 
+    // The argument block (some 560 bytes) is read throughout the setup below
+    // in chains of dependent scalar loads, and it starts every launch outside
+    // the scalar cache: touch each of its 64-byte lines first, all loads in
+    // flight together, so the chains then hit the cache instead of paying a
+    // miss per line in turn.
+    {
+        const auto *ka = (const __attribute__((address_space(4))) uint32_t *)
+            __builtin_amdgcn_kernarg_segment_ptr();
+        constexpr int kWords = (int)(sizeof(LayerArgs) / 4);
+        static_assert(kWords <= 160, "ten 64-byte lines");
+        uint32_t t[10];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) t[i] = ka[min(16 * i, kWords - 1)];
+        asm volatile("" : : "s"(t[0]), "s"(t[1]), "s"(t[2]), "s"(t[3]), "s"(t[4]),
+                     "s"(t[5]), "s"(t[6]), "s"(t[7]), "s"(t[8]), "s"(t[9]));
+    }
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int h = lane / 16;
@@ -207,6 +223,19 @@ void layer_dot4_kernel(LayerArgs a) {
     }
     const bool has_work = nit > 0 && tile_of(0) < total;
 
+    // Weight scales, one per projection in its packed tail: lane p < 7 of
+    // wave 0 loads scale p.  A divergent address makes it a vector load,
+    // issued first and waited for only where the scales are written to LDS at
+    // the end of the prologue: a scalar load of these cold lines would share
+    // the counter that the prologue's barriers wait on for LDS, and every
+    // workgroup would sit out an HBM round trip before quantizing.
+    const int sp = min(lane, kLayerProj - 1);
+    const int64_t code_bytes = B3 ? b3_code_bytes(sel(a.M, sp), sel(a.K, proj_group(sp)))
+                                  : sel(a.M, sp) * sel(a.K, proj_group(sp)) / 4;
+    float wsl = 0.0f;
+    if (wave == 0)
+        wsl = *to_global(reinterpret_cast<const float *>(sel(a.packed, sp) + code_bytes));
+
     // ---- prologue, part 1: this wave's input chunks into registers ----
     // Wave w owns chunks [w * kSpan, (w + 1) * kSpan) of the sequence; lane l
     // holds chunks w * kSpan + 64c + l (c < kLayerUnits), so every load is one
@@ -269,11 +298,6 @@ void layer_dot4_kernel(LayerArgs a) {
         raw[c].load(d < nlive ? src + 8 * d : last);
         rowof[c] = r;
     }
-    // Weight scale of projection min(wave, 6) (from its packed tail).
-    const int wp = min(wave, kLayerProj - 1);
-    const int64_t code_bytes = B3 ? b3_code_bytes(sel(a.M, wp), sel(a.K, proj_group(wp)))
-                                  : sel(a.M, wp) * sel(a.K, proj_group(wp)) / 4;
-    const float ws = *to_global(reinterpret_cast<const float *>(sel(a.packed, wp) + code_bytes));
     if (threadIdx.x < kKeys) {
         s_amax[threadIdx.x] = 0;
         s_sum[threadIdx.x] = 0;
@@ -411,7 +435,7 @@ void layer_dot4_kernel(LayerArgs a) {
             }
         }
     }
-    if (wave < kLayerProj && lane == 0) s_ws[wave] = ws;
+    if (wave == 0 && lane < kLayerProj) s_ws[lane] = wsl;
     __syncthreads();
 
     // ---- tiles ----
