@@ -95,6 +95,7 @@ template <>
 struct Chunk<uint16_t> {
     v4u a;
     __device__ __forceinline__ void load(const uint16_t *p) { a = *to_global(reinterpret_cast<const v4u *>(p)); }
+    __device__ __forceinline__ void clear() { a = v4u{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ uint32_t abs_bits() const {
         uint32_t r = 0;
         const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -280,23 +281,34 @@ void layer_dot4_kernel(LayerArgs a) {
             }
         }
     }
-    // Dead chunks (past the sequence) re-read the last chunk of the last row.
+    // Dead lanes (past the sequence) re-read the last chunk of the last row;
+    // a wave with no live chunk issues no load (the prologue's loads queue
+    // behind one another, and at one 70B-class token three of the 16 waves
+    // hold nothing).
     const T *last = static_cast<const T *>(a.x[kLayerInputs - 1]) +
                     a.N * a.K[kLayerInputs - 1] - 8;
     Chunk<T> raw[kLayerUnits];
     int rowof[kLayerUnits];
+    if (nlive == 0) {
 #pragma unroll
-    for (int c = 0; c < kLayerUnits; ++c) {
-        const int d = kWave * c + lane;
-        int r = 0;
-        const T *src = rsrc[0];
-#pragma unroll
-        for (int k = 1; k < kWaveRows; ++k) {
-            r += d >= st[k] ? 1 : 0;
-            src = d >= st[k] ? rsrc[k] : src;
+        for (int c = 0; c < kLayerUnits; ++c) {
+            raw[c].clear();
+            rowof[c] = 0;
         }
-        raw[c].load(d < nlive ? src + 8 * d : last);
-        rowof[c] = r;
+    } else {
+#pragma unroll
+        for (int c = 0; c < kLayerUnits; ++c) {
+            const int d = kWave * c + lane;
+            int r = 0;
+            const T *src = rsrc[0];
+#pragma unroll
+            for (int k = 1; k < kWaveRows; ++k) {
+                r += d >= st[k] ? 1 : 0;
+                src = d >= st[k] ? rsrc[k] : src;
+            }
+            raw[c].load(d < nlive ? src + 8 * d : last);
+            rowof[c] = r;
+        }
     }
     if (threadIdx.x < kKeys) {
         s_amax[threadIdx.x] = 0;
