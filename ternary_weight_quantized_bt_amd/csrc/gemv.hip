@@ -140,6 +140,10 @@ void decode_dot4_kernel(GroupArgs a, DecodeX dx) {
     // ---- prologue, part 1: global loads of the activations ----
     // They are issued before the first ring fill, so they return first and
     // the activation staging below overlaps the HBM latency of the weights.
+    // With the quantization fused (MODE 0) the ring fill waits until after
+    // the absmax barrier: issued earlier, it queues with the activation loads
+    // and holds up every wave's arrival there (2.3 % on the 70B-class block
+    // as four launches).
     constexpr int kUnits = sizeof(Raw8<T>) / 16;
     constexpr int kChunks = kRawUnits / (NT * kUnits);  // MODE 0: raw chunks
     constexpr int kCopy = (int)((kDecLdsMax + 16 * kThreads - 1) / (16 * kThreads));  // MODE 1
@@ -166,18 +170,27 @@ void decode_dot4_kernel(GroupArgs a, DecodeX dx) {
         }
     }
 
+    // Weight scales of the group's projections: loaded before the ring fill
+    // and written to LDS at the end of the prologue, so that no wait for them
+    // also waits for the ring's HBM round trip (the vector-memory counter
+    // retires in order).
+    float wsc = 0.0f;
+    if (threadIdx.x < kMaxGroup) wsc = group_weight_scale(a, threadIdx.x);
+
     // First ring fill.
     v4u ring[RING];
-    if (has_work) {
+    auto fill = [&]() {
+        if (has_work) {
 #pragma unroll
-        for (int d = 0; d < RING; ++d) {
-            ring[d] = __builtin_nontemporal_load(lp);
-            advance_load();
+            for (int d = 0; d < RING; ++d) {
+                ring[d] = __builtin_nontemporal_load(lp);
+                advance_load();
+            }
         }
-    }
+    };
+    if (MODE != 0) fill();
 
     // ---- prologue, part 2: int8 activations of every token into LDS ----
-    if (threadIdx.x < kMaxGroup) s_wscale[threadIdx.x] = group_weight_scale(a, threadIdx.x);
     const int8_t *xsrc;
     if (MODE == 0) {
         float amax[NT];
@@ -191,6 +204,7 @@ void decode_dot4_kernel(GroupArgs a, DecodeX dx) {
             if (lane == 0) s_amax[wave][j] = mb;
         }
         __syncthreads();
+        fill();
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             uint32_t mb = s_amax[0][j];
@@ -240,6 +254,7 @@ void decode_dot4_kernel(GroupArgs a, DecodeX dx) {
         }
         xsrc = dx.xq;
     }
+    if (threadIdx.x < kMaxGroup) s_wscale[threadIdx.x] = wsc;
     __syncthreads();
     // dequantization factor per (projection, token)
     if (threadIdx.x < kMaxGroup * NT) {
