@@ -47,11 +47,13 @@ namespace {
 // (four tiles per iteration), 4 slot loads in flight per wave.  At 8 tokens
 // of the 70B-class block this is 6 % faster than 8 waves with a 4-way split
 // and 9 % faster than 8 waves with an 8-way split; 12 waves, 2- or 8-way
-// splits and rings of 3 or 6 were slower or equal.
+// splits were slower or equal.  With non-temporal weight loads a ring of 3
+// slots per wave is the fastest at 8 tokens (2 / 3 / 4 / 5: 3.62 / 3.56 /
+// 3.65 / 3.74 ms per 80 blocks in alternating runs).
 constexpr int kMfWaves = 16;
 constexpr int kMfThreads = kMfWaves * kWave;
 constexpr int kMfSplit = 4;
-constexpr int kMfRing = 4;
+constexpr int kMfRing = 3;
 // LDS of one compute unit and the part a workgroup may use for token codes.
 constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kMfCodesMax = 128 * 1024;
