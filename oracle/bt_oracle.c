@@ -43,9 +43,13 @@
  *       xq = clamp(round-half-even(x * inv), -127, 127) with a binary32
  *       multiply; the token's scale is amax; amax == 0 gives xq = 0 and
  *       scale 0.  When amax is so small (below 127 / FLT_MAX) that 127 / amax
- *       overflows to infinity, x * inv is +-infinity for x != 0 and 0 * inf
- *       is undefined; the reading takes the limit of the formula: xq = 127 *
- *       sign(x), and 0 for x == 0.
+ *       overflows, the same binary32 steps are kept with inv = +infinity:
+ *       x * inv is +-infinity for x != 0, which the clamp turns into
+ *       127 * sign(x), and the one undefined product, 0 * infinity (NaN in
+ *       IEEE arithmetic), is defined here as 0.  This is a convention for
+ *       inputs the pages never consider, not the real-number value of
+ *       x * 127 / amax (for x = 2e-38, amax = 1e-37 that is 25.4, while this
+ *       gives 127).
  *   R6  The contraction is carried out in integers and dequantized once:
  *       y = acc * s_w * s_a / 127 ([I2S] "How I2_S Kernels Process the
  *       Format" multiplies by the shared per-tensor scale; a per-tensor
@@ -166,7 +170,7 @@ static void bto_quant_token(const float *x, int64_t K,
     float inv = 127.0f / amax;               /* binary32, correctly rounded */
     for (int64_t k = 0; k < K; ++k) {
         float p = x[k] * inv;                /* binary32 product */
-        if (isinf(inv) && x[k] == 0.0f) p = 0.0f;  /* R5: limit, not 0 * inf */
+        if (isinf(inv) && x[k] == 0.0f) p = 0.0f;  /* R5: 0 * inf := 0 */
         float r = rintf(p);                  /* round half to even */
         if (r > 127.0f) r = 127.0f;
         if (r < -127.0f) r = -127.0f;

@@ -7,8 +7,9 @@
 // pages print no formula; the one implemented (stated in libternary.h):
 //   amax = max|x| (float32; exact in any order), inv = 127 / amax (float32,
 //   correctly rounded), xq = clamp(rne(x * inv), -127, 127) with a float32
-//   multiply and round-half-to-even, scale = amax, sum = sum of xq (and the
-//   limit 127 * sign(x) where 127 / amax overflows).
+//   multiply and round-half-to-even, scale = amax, sum = sum of xq.  Where
+//   127 / amax overflows, inv = +infinity and the same steps give
+//   127 * sign(x) after the clamp, with 0 * infinity taken as 0.
 // __fdiv_rn / __fmul_rn / __fadd_rn pin the division, the product and the
 // rounding addition whatever the compiler flags (no contraction into fma).
 #pragma once
@@ -123,9 +124,9 @@ __device__ __forceinline__ uint32_t quant1(float x, float inv) {
     return __float_as_uint(__fadd_rn(__fmul_rn(x, inv), 12582912.0f));
 }
 
-// The code for an infinite inv (amax below 127 / FLT_MAX): the limit
-// 127 * sign(x), and 0 for x == 0.
-__device__ __forceinline__ uint32_t quant1_limit(float x) {
+// The code for an infinite inv (amax below 127 / FLT_MAX): x * inf clamped,
+// i.e. 127 * sign(x), and 0 for x == 0 (0 * inf taken as 0).
+__device__ __forceinline__ uint32_t quant1_inf(float x) {
     return x > 0.0f ? 127u : (x < 0.0f ? 0xFFFFFF81u : 0u);
 }
 
@@ -162,7 +163,7 @@ __device__ __forceinline__ uint2 quant8(const Eight &e, float inv, int &sum) {
     if (__builtin_expect(__builtin_isinf(inv), 0)) {
         uint32_t q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = quant1_limit(e.v[i]);
+        for (int i = 0; i < 8; ++i) q[i] = quant1_inf(e.v[i]);
         return pack8(q, sum);
     }
     return quant8_finite(e, inv, sum);

@@ -90,9 +90,10 @@ def test_fused_block_repeated_calls_and_zero_token():
 
 
 @pytest.mark.parametrize("wl", [SPLIT8, SPLIT16], ids=lambda w: w.name)
-def test_fused_block_tiny_token_takes_the_limit(wl):
-    """A token whose 127 / amax overflows (inputs ~1e-39): codes are
-    127 * sign(x) on both launch structures and match the oracle."""
+def test_fused_block_tiny_token_infinite_reciprocal(wl):
+    """A token whose 127 / amax overflows (inputs ~1e-39): inv = +inf, so the
+    codes are 127 * sign(x) (0 * inf taken as 0) on both launch structures
+    and match the oracle."""
     ws, packed, L = build(wl)
     xs = W.layer_inputs(wl, 0, 2)
     xs[0] = xs[0].float()

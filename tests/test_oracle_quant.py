@@ -87,10 +87,12 @@ def test_subnormals_quantize_to_zero_without_amax_change():
     assert s[0] == 1.0
 
 
-def test_overflowing_reciprocal_takes_the_limit():
-    # amax below 127 / FLT_MAX: 127 / amax is +inf in binary32, so every
-    # nonzero x maps to 127 * sign(x) (the limit of x * 127 / amax, clamped)
-    # and x == 0 to 0, whether amax is normal or subnormal.
+def test_overflowing_reciprocal_keeps_binary32_steps():
+    # amax below 127 / FLT_MAX: 127 / amax is +inf in binary32, so x * inv is
+    # +-inf for every nonzero x and the clamp gives 127 * sign(x); 0 * inf is
+    # taken as 0.  Whether amax is normal or subnormal.  This is not the real
+    # value of x * 127 / amax: 2e-38 * 127 / 1e-37 = 25.4 (row 0, column 3)
+    # still gets 127.
     with np.errstate(over="ignore"):
         assert np.isinf(np.float32(127.0) / np.float32(1e-37))
     x = np.array([[1e-37, -5e-38, 0.0, 2e-38, -0.0],
