@@ -35,6 +35,16 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
           "-fopenmp", "-shared", "-fPIC"]
+# A checking build of the same source (host code only): address and
+# undefined-behaviour sanitizers, float-to-int conversions out of range
+# included, every report fatal.  Loading it needs the address sanitizer's
+# runtime preloaded into the process.
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer",
+                  "-fsanitize=address,undefined,float-cast-overflow",
+                  "-fno-sanitize-recover=all"]
+# Set to the path of another build of bt_oracle.c (e.g. the checking build)
+# to load that one instead.
+LIB_ENV = "BT_ORACLE_SO"
 
 _lib = None
 
@@ -48,13 +58,22 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile bt_oracle.c with SANITIZE_FLAGS into `path`."""
+    subprocess.run(["gcc", *CFLAGS, *SANITIZE_FLAGS, "-o", path, _SRC, "-lm"], check=True)
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or (
-                os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get(LIB_ENV)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or (
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int64
         lib.bto_packed_bytes.argtypes = [I, I]

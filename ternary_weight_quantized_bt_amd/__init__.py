@@ -182,6 +182,30 @@ def _check(status: int):
         raise BtError(status, lib().bt_last_error().decode())
 
 
+def _keep_for_stream(tensors, stream):
+    """Tensors allocated here on the current stream but used by kernels on
+    another stream: tell torch's caching allocator, so their memory is not
+    handed out again before that stream's work is done."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None and t.numel():
+            t.record_stream(s)
+
+
+def _out(out, shape, dtype, device, what):
+    """A caller-supplied output tensor (checked), or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype:
+        raise ValueError(f"{what}: expected {tuple(shape)} {dtype}, got "
+                         f"{tuple(out.shape)} {out.dtype}")
+    return out
+
+
 # ---------------------------------------------------------------- C ABI ----
 
 def bt_abi_version() -> int:
@@ -298,67 +322,74 @@ def bt_layer_forward(layer: bt_layer, io: bt_layer_io, stream=None):
 
 # -------------------------------------------------------------- helpers ----
 
-def pack(w: torch.Tensor, scale: float, invalid_count=None, stream=None):
+def _check_packed(packed, n, what):
+    if packed.dtype != torch.uint8 or packed.numel() != n:
+        raise ValueError(f"{what}: packed weights must be {n} uint8 bytes, got "
+                         f"{packed.numel()} {packed.dtype}")
+
+
+def pack(w: torch.Tensor, scale: float, invalid_count=None, stream=None, out=None):
     """int8 [M, K] device tensor -> packed uint8 device tensor."""
     M, K = w.shape
     n = bt_packed_bytes(M, K)
     if n == 0:
         raise BtError(BT_ERR_SHAPE, bt_last_error())
-    packed = torch.empty(n, dtype=torch.uint8, device=w.device)
+    packed = _out(out, (n,), torch.uint8, w.device, "pack")
     bt_pack_ternary(w, M, K, scale, packed, invalid_count, stream)
     return packed
 
 
-def unpack(packed: torch.Tensor, M: int, K: int, stream=None):
-    w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
+def unpack(packed: torch.Tensor, M: int, K: int, stream=None, out=None):
+    w = _out(out, (M, K), torch.int8, packed.device, "unpack")
     bt_unpack_ternary(packed, M, K, w, stream)
     return w
 
 
-def pack_b3(w: torch.Tensor, scale: float, invalid_count=None, stream=None):
+def pack_b3(w: torch.Tensor, scale: float, invalid_count=None, stream=None, out=None):
     """int8 [M, K] device tensor -> base-3 B3T1024 packed uint8 device tensor."""
     M, K = w.shape
     n = bt_b3_bytes(M, K)
     if n == 0:
         raise BtError(BT_ERR_SHAPE, bt_last_error())
-    packed = torch.empty(n, dtype=torch.uint8, device=w.device)
+    packed = _out(out, (n,), torch.uint8, w.device, "pack_b3")
     bt_pack_ternary_b3(w, M, K, scale, packed, invalid_count, stream)
     return packed
 
 
-def unpack_b3(packed: torch.Tensor, M: int, K: int, stream=None):
-    w = torch.empty((M, K), dtype=torch.int8, device=packed.device)
+def unpack_b3(packed: torch.Tensor, M: int, K: int, stream=None, out=None):
+    w = _out(out, (M, K), torch.int8, packed.device, "unpack_b3")
     bt_unpack_ternary_b3(packed, M, K, w, stream)
     return w
 
 
-def dequantize(packed: torch.Tensor, M: int, K: int, dtype=torch.float32, stream=None):
+def dequantize(packed: torch.Tensor, M: int, K: int, dtype=torch.float32, stream=None,
+               out=None):
     """Packed weights -> float32 / bfloat16 [M, K] device tensor
     ((code - 1) * scale)."""
-    w = torch.empty((M, K), dtype=dtype, device=packed.device)
+    w = _out(out, (M, K), dtype, packed.device, "dequantize")
     bt_dequantize_weights(packed, M, K, w, _BT_DTYPE[dtype], stream)
     return w
 
 
 def i2s_import(i2s: torch.Tensor, M: int, K: int, block: int, invalid_count=None,
-               stream=None):
+               stream=None, out=None):
     """I2_S bytes (blocks of `block` weights) -> packed T16Q256 tensor."""
     n = bt_packed_bytes(M, K)
     if n == 0:
         raise BtError(BT_ERR_SHAPE, bt_last_error())
-    packed = torch.empty(n, dtype=torch.uint8, device=i2s.device)
+    packed = _out(out, (n,), torch.uint8, i2s.device, "i2s_import")
     bt_i2s_import(i2s, M, K, block, packed, invalid_count, stream)
     return packed
 
 
-def i2s_export(packed: torch.Tensor, M: int, K: int, block: int, stream=None):
+def i2s_export(packed: torch.Tensor, M: int, K: int, block: int, stream=None, out=None):
     """Packed T16Q256 tensor -> I2_S bytes (blocks of `block` weights)."""
     n = bt_i2s_bytes(M, K)
     if n == 0:
         raise BtError(BT_ERR_SHAPE, bt_last_error())
-    out = torch.empty(n, dtype=torch.uint8, device=packed.device)
-    bt_i2s_export(packed, M, K, block, out, stream)
-    return out
+    res = _out(out, (n,), torch.uint8, packed.device, "i2s_export")
+    bt_i2s_export(packed, M, K, block, res, stream)
+    return res
 
 
 def quantize_weights(w: torch.Tensor, mode: str = "absmean", eps: float = 0.0,
@@ -380,38 +411,47 @@ def quantize_weights(w: torch.Tensor, mode: str = "absmean", eps: float = 0.0,
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     bt_quantize_weights(w, _BT_DTYPE[w.dtype], M, K, modes[mode], eps, packed, stats,
                         ws, ws_bytes, stream)
+    _keep_for_stream((ws, packed, stats), stream)
     return packed, stats
 
 
-def quant_act(x: torch.Tensor, stream=None):
-    """float32 / bfloat16 [N, K] -> (xq int8 [N, K], scale f32 [N], sum i32 [N])."""
+def quant_act(x: torch.Tensor, stream=None, out=None):
+    """float32 / bfloat16 [N, K] -> (xq int8 [N, K], scale f32 [N], sum i32 [N]);
+    out, if given, is such a triple to write into."""
     N, K = x.shape
     dev = x.device
-    xq = torch.empty((N, K), dtype=torch.int8, device=dev)
-    s = torch.empty(N, dtype=torch.float32, device=dev)
-    sm = torch.empty(N, dtype=torch.int32, device=dev)
+    o = out if out is not None else (None, None, None)
+    xq = _out(o[0], (N, K), torch.int8, dev, "quant_act xq")
+    s = _out(o[1], (N,), torch.float32, dev, "quant_act scale")
+    sm = _out(o[2], (N,), torch.int32, dev, "quant_act sum")
     bt_quant_act(x, _BT_DTYPE[x.dtype], N, K, xq, s, sm, stream)
     return xq, s, sm
 
 
-def _matmul(fn, packed, M, K, xq, xs, xsum, y_dtype, stream):
+def _matmul(fn, packed, M, K, xq, xs, xsum, y_dtype, stream, y, b3=False):
     N = xq.shape[0]
-    y = torch.empty((N, M), dtype=_TORCH_DTYPE[y_dtype], device=xq.device)
+    if tuple(xq.shape) != (N, K) or xq.dtype != torch.int8:
+        raise ValueError(f"xq must be int8 [N, {K}], got {tuple(xq.shape)} {xq.dtype}")
+    if tuple(xs.shape) != (N,) or tuple(xsum.shape) != (N,):
+        raise ValueError("x_scale and x_sum must have one entry per token")
+    _check_packed(packed, bt_b3_bytes(M, K) if b3 else bt_packed_bytes(M, K), "matmul")
+    y = _out(y, (N, M), _TORCH_DTYPE[y_dtype], xq.device, "matmul y")
     fn(packed, M, K, xq, xs, xsum, N, y, y_dtype, stream)
     return y
 
 
-def gemv(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
-    return _matmul(bt_ternary_gemv, packed, M, K, xq, xs, xsum, y_dtype, stream)
+def gemv(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None, y=None):
+    return _matmul(bt_ternary_gemv, packed, M, K, xq, xs, xsum, y_dtype, stream, y)
 
 
-def gemv_b3(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
+def gemv_b3(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None, y=None):
     """The decode product over base-3 B3T1024 weights (same results as gemv)."""
-    return _matmul(bt_ternary_gemv_b3, packed, M, K, xq, xs, xsum, y_dtype, stream)
+    return _matmul(bt_ternary_gemv_b3, packed, M, K, xq, xs, xsum, y_dtype, stream, y,
+                   b3=True)
 
 
-def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None):
-    return _matmul(bt_ternary_gemm, packed, M, K, xq, xs, xsum, y_dtype, stream)
+def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None, y=None):
+    return _matmul(bt_ternary_gemm, packed, M, K, xq, xs, xsum, y_dtype, stream, y)
 
 
 class Layer:
@@ -425,6 +465,8 @@ class Layer:
         self.base3 = base3
         self.c = bt_layer()
         for p, (t, (M, K)) in enumerate(zip(self.packed, self.shapes)):
+            _check_packed(t, bt_b3_bytes(M, K) if base3 else bt_packed_bytes(M, K),
+                          f"layer projection {p}")
             self.c.w[p] = _p(t)
             self.c.M[p] = M
             self.c.K[p] = K
@@ -456,14 +498,40 @@ class Layer:
         return torch.empty(max(self.workspace_bytes(N), 256), dtype=torch.uint8,
                            device=device)
 
+    def input_widths(self):
+        """K of the four inputs (q/k/v, o, gate/up, down)."""
+        return [self.shapes[0][1], self.shapes[3][1], self.shapes[4][1], self.shapes[6][1]]
+
+    def check_io(self, xs, ys, y_dtype):
+        """Shapes, dtypes and devices of the inputs and outputs: a mismatch
+        would make the kernels read or write out of bounds."""
+        if len(xs) != BT_LAYER_INPUTS:
+            raise ValueError(f"need {BT_LAYER_INPUTS} inputs, got {len(xs)}")
+        N, dt = xs[0].shape[0], xs[0].dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"inputs must be float32 or bfloat16, got {dt}")
+        for i, (x, K) in enumerate(zip(xs, self.input_widths())):
+            if x.dim() != 2 or tuple(x.shape) != (N, K) or x.dtype != dt or not x.is_cuda:
+                raise ValueError(f"input {i}: expected a GPU tensor [{N}, {K}] {dt}, got "
+                                 f"{tuple(x.shape)} {x.dtype} on {x.device}")
+        if len(ys) != BT_LAYER_PROJ:
+            raise ValueError(f"need {BT_LAYER_PROJ} outputs, got {len(ys)}")
+        for p, (y, (M, _)) in enumerate(zip(ys, self.shapes)):
+            if tuple(y.shape) != (N, M) or y.dtype != _TORCH_DTYPE[y_dtype] or not y.is_cuda:
+                raise ValueError(f"output {p}: expected a GPU tensor [{N}, {M}] "
+                                 f"{_TORCH_DTYPE[y_dtype]}, got {tuple(y.shape)} {y.dtype}")
+
     def forward(self, xs, y_dtype=BT_BF16, ys=None, workspace=None, stream=None,
                 per_group=False):
         N = xs[0].shape[0]
         dev = xs[0].device
-        if ys is None:
+        own_ws, own_ys = workspace is None, ys is None
+        if own_ys:
             ys = self.alloc_outputs(N, y_dtype, dev)
-        if workspace is None:
+        self.check_io(xs, ys, y_dtype)
+        if own_ws:
             workspace = self.alloc_workspace(N, dev)
         io = self.make_io(xs, ys, y_dtype, workspace, per_group)
         bt_layer_forward(self.c, io, stream)
+        _keep_for_stream(([workspace] if own_ws else []) + (list(ys) if own_ys else []), stream)
         return ys

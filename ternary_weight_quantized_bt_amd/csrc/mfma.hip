@@ -44,7 +44,7 @@ namespace bt {
 namespace {
 
 // Launch shape: 16 waves per workgroup, a tile's K split over 4 of them
-// (four tiles per iteration), 4 slot loads in flight per wave.  At 8 tokens
+// (four tiles per iteration), 3 slot loads in flight per wave.  At 8 tokens
 // of the 70B-class block this is 6 % faster than 8 waves with a 4-way split
 // and 9 % faster than 8 waves with an 8-way split; 12 waves, 2- or 8-way
 // splits were slower or equal.  With non-temporal weight loads a ring of 3
@@ -304,6 +304,15 @@ void decode_mfma_multi_kernel(MultiArgs m) {
         mfma_group<WAVES, P, RING>(m.g[3], m.nph[3], m.qph[3], b - m.start[3], m.start[4] - m.start[3]);
 }
 
+// Static LDS of a kernel as compiled (the partial-sum buffers and the token
+// table), read once per kernel: the dynamic part must fit beside it.
+template <typename Kern>
+int64_t static_lds(Kern kern) {
+    hipFuncAttributes attr{};
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kern)) != hipSuccess) return -1;
+    return (int64_t)attr.sharedSizeBytes;
+}
+
 hipError_t launch_mf(const GroupArgs &a, int nph, int qph, int64_t grid, size_t shmem,
                      hipStream_t s) {
     auto kern = decode_mfma_kernel<kMfWaves, kMfSplit, kMfRing>;
@@ -319,17 +328,17 @@ hipError_t launch_mf(const GroupArgs &a, int nph, int qph, int64_t grid, size_t 
     return hipGetLastError();
 }
 
-// K phases of a group: as few as keep one phase's codes within kMfCodesMax.
+// K phases of a group: as few as keep one phase's codes within `cap` bytes.
 struct Plan {
     int64_t nph, qph, codes, groups;
 };
-Plan plan_group(const GroupArgs &a) {
+Plan plan_group(const GroupArgs &a, int64_t cap = kMfCodesMax) {
     constexpr int TPW = kMfWaves / kMfSplit;
     Plan p;
     const int64_t rows = min((int64_t)16, a.N);
     const int64_t qb = a.K / kTileCols;
     const int64_t per_block = rows * kTileCols;
-    const int64_t max_blocks = max((int64_t)1, kMfCodesMax / per_block);
+    const int64_t max_blocks = max((int64_t)1, cap / per_block);
     p.nph = (qb + max_blocks - 1) / max_blocks;
     p.qph = (qb + p.nph - 1) / p.nph;
     p.codes = (rows * p.qph * kTileCols + 1023) / 1024 * 1024;
@@ -337,37 +346,57 @@ Plan plan_group(const GroupArgs &a) {
     return p;
 }
 
-// With more than one phase, at most kMfPhaseTiles iterations per workgroup
-// keep their partial sums: the grid is at least groups / kMfPhaseTiles, and
-// the partial sums take nit_max KiB per tile of an iteration.
-int64_t phase_grid(const Plan &p, int64_t grid) {
-    return p.nph > 1 ? max(grid, (p.groups + kMfPhaseTiles - 1) / kMfPhaseTiles) : grid;
-}
+// Partial sums of one iteration's tiles (1 KiB per tile) with more than one
+// phase; a workgroup keeps those of each of its iterations.
+constexpr int64_t kMfIterPartial = (kMfWaves / kMfSplit) * kWave * 16;
+
 int64_t partial_bytes(const Plan &p, int64_t grid) {
-    constexpr int TPW = kMfWaves / kMfSplit;
     if (p.nph <= 1) return 0;
-    return (p.groups + grid - 1) / grid * TPW * kWave * 16;
+    return (p.groups + grid - 1) / grid * kMfIterPartial;
 }
 
-// static LDS: partial sums of the waves (double-buffered, P - 1 parts per
-// tile of an iteration) and the token table
-constexpr int64_t kMfFixedLds =
-    2 * (kMfWaves / kMfSplit) * (kMfSplit > 1 ? kMfSplit - 1 : 1) * kWave * 16 + 256;
+// Makes the group's codes plus partial sums fit `avail` bytes of dynamic LDS
+// with a grid of at least `grid` workgroups.  With more than one phase a
+// workgroup keeps the partial sums of at most kMfPhaseTiles iterations, and
+// of fewer when the codes leave less room (the grid grows instead); when not
+// even one iteration's partial sums fit beside the codes, the phases get
+// shorter.  Returns false if no plan fits.
+bool fit_plan(const GroupArgs &a, Plan &p, int64_t &grid, int64_t avail) {
+    for (int64_t cap = kMfCodesMax; cap >= (int64_t)kTileCols; cap -= 16 * 1024) {
+        Plan q = plan_group(a, cap);
+        if (q.nph <= 1) {
+            if (q.codes > avail) continue;
+            p = q;
+            return true;
+        }
+        const int64_t its = min(kMfPhaseTiles, (avail - q.codes) / kMfIterPartial);
+        if (its < 1) continue;
+        p = q;
+        grid = min(max(grid, (p.groups + its - 1) / its), p.groups);
+        return true;
+    }
+    return false;
+}
 
 }  // namespace
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     if (a.N <= 0 || group_tiles(a) == 0) return hipSuccess;
-    const Plan p = plan_group(a);
+    static const int64_t stat = static_lds(decode_mfma_kernel<kMfWaves, kMfSplit, kMfRing>);
+    if (stat < 0) return hipErrorInvalidDeviceFunction;
+    Plan p = plan_group(a);
     const int64_t tgroups = (a.N + 15) / 16;
-    const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (p.codes + kMfFixedLds)));
+    const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (p.codes + stat)));
     int64_t grid = max((int64_t)1, min(p.groups, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups));
-    grid = phase_grid(p, grid);
+    if (!fit_plan(a, p, grid, kLdsPerCu - stat)) return hipErrorInvalidConfiguration;
     return launch_mf(a, (int)p.nph, (int)p.qph, grid, (size_t)(p.codes + partial_bytes(p, grid)), s);
 }
 
 hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
     if (count < 1 || count > kMaxMulti) return hipErrorInvalidValue;
+    auto kern = decode_mfma_multi_kernel<kMfWaves, kMfSplit, kMfRing>;
+    static const int64_t stat = static_lds(kern);
+    if (stat < 0) return hipErrorInvalidDeviceFunction;
     GroupArgs gs[kMaxMulti];
     for (int i = 0; i < count; ++i) gs[i] = make_group_args(groups[i]);
     const int64_t N = gs[0].N;
@@ -384,9 +413,11 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
     const int64_t tgroups = (N + 15) / 16;
     // Workgroups per compute unit from the largest group's codes, then the
     // grid split over the groups in proportion to their weight bytes (they
-    // run side by side and end together); one more pass if the partial sums
-    // of the phased groups leave room for fewer workgroups per unit.
-    int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (codes_max + kMfFixedLds)));
+    // run side by side and end together), each share raised where its
+    // partial sums need it (fit_plan); one more pass if the dynamic LDS then
+    // leaves room for fewer workgroups per unit.  Dynamic plus static LDS
+    // stays within one compute unit's.
+    int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (codes_max + stat)));
     int64_t grid[kMaxMulti] = {};
     int64_t shmem = 0;
     for (int pass = 0; pass < 2; ++pass) {
@@ -394,13 +425,15 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
         shmem = 0;
         for (int i = 0; i < count; ++i) {
             const int64_t share = (budget * bytes[i] + total / 2) / total;
-            grid[i] = phase_grid(p[i], max((int64_t)1, min(p[i].groups, share)));
+            grid[i] = max((int64_t)1, min(p[i].groups, share));
+            if (!fit_plan(gs[i], p[i], grid[i], kLdsPerCu - stat)) return hipErrorInvalidConfiguration;
             shmem = max(shmem, p[i].codes + partial_bytes(p[i], grid[i]));
         }
-        const int fit = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (shmem + kMfFixedLds)));
+        const int fit = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (shmem + stat)));
         if (fit >= per_cu) break;
         per_cu = fit;
     }
+    if (shmem + stat > kLdsPerCu) return hipErrorInvalidConfiguration;
     MultiArgs m{};
     int64_t start = 0;
     for (int i = 0; i < kMaxMulti; ++i) {
@@ -412,7 +445,6 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
         if (i < count) start += grid[i];
     }
     m.start[kMaxMulti] = (int)start;
-    auto kern = decode_mfma_multi_kernel<kMfWaves, kMfSplit, kMfRing>;
     if (shmem > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -53,3 +53,41 @@ def check_projection(packed_gpu, packed_ref, M, K, xq_ref, xs_ref, acc_ref_rows,
     else:
         ref = oracle.dequant(acc_ref_rows, oracle.scale_of(packed_ref, M, K), xs_ref)
         assert_rel_close(as_f64(y), ref, RTOL[ydt], what)
+
+
+# ------------------------------------------------------------ canaries ----
+
+GUARD = 4096      # sentinel bytes before and after each guarded output
+SENTINEL = 0xA5
+
+_ELEM = {torch.int8: 1, torch.uint8: 1, torch.bfloat16: 2, torch.int16: 2,
+         torch.float32: 4, torch.int32: 4}
+
+
+class Guarded:
+    """An output tensor with GUARD sentinel bytes on each side, in one
+    allocation (the output itself starts 16-byte aligned and filled with the
+    sentinel): a kernel that writes past either end of its output changes a
+    sentinel byte, which check() reports."""
+
+    def __init__(self, shape, dtype, device="cuda:0"):
+        n = int(np.prod(shape)) * _ELEM[dtype]
+        self.n = n
+        self.buf = torch.full((2 * GUARD + (n + 15) // 16 * 16,), SENTINEL,
+                              dtype=torch.uint8, device=device)
+        self.t = self.buf[GUARD:GUARD + n].view(dtype).view(*shape)
+
+    def check(self, what=""):
+        b = self.buf.cpu().numpy()
+        front, back = b[:GUARD], b[GUARD + self.n:]
+        for name, band in (("before", front), ("after", back)):
+            bad = np.flatnonzero(band != SENTINEL)
+            if bad.size:
+                raise AssertionError(f"{what}: {bad.size} sentinel bytes {name} the output "
+                                     f"changed (first at band offset {bad[0]})")
+
+
+def guarded(shape, dtype, device="cuda:0"):
+    """A Guarded output and its tensor."""
+    g = Guarded(shape, dtype, device)
+    return g, g.t

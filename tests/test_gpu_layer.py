@@ -8,7 +8,7 @@ import torch
 import oracle
 import ternary_weight_quantized_bt_amd as bt
 import workloads as W
-from parity import (RTOL, as_f64, assert_equal, assert_rel_close,
+from parity import (RTOL, Guarded, as_f64, assert_equal, assert_rel_close,
                     check_projection, to_np, x_for_oracle)
 
 pytestmark = [pytest.mark.gpu,
@@ -25,27 +25,52 @@ SMALL = W.Workload(
     weight_dist="p0_0.4", act_dist="normal", outlier_frac=0.01, outlier_scale=20.0)
 
 
-def run_layer(wl, layer, N, ydt, rows_per_proj=None, seed_rows=0):
-    """Build one layer on the GPU, run the driver, compare with the oracle."""
+TORCH_DT = {bt.BT_I32: torch.int32, bt.BT_F32: torch.float32, bt.BT_BF16: torch.bfloat16}
+
+
+def sample_rows(rng, M, count):
+    """`count` random rows of M plus the first and the last 16-row tile (the
+    projection's edges in a launch that lays several projections end to end)."""
+    if count is None or count >= M:
+        return None
+    edges = np.r_[np.arange(16), np.arange(M - 16, M)]
+    return np.unique(np.r_[rng.choice(M, count, replace=False), edges])
+
+
+def forward_guarded(L, wl, xs, N, ydt, per_group=False):
+    """L.forward into outputs between sentinel bands; checks the bands."""
+    gs = [Guarded((N, M), TORCH_DT[ydt]) for (M, _) in wl.shapes]
+    ys = L.forward(xs, y_dtype=ydt, ys=[g.t for g in gs], per_group=per_group)
+    torch.cuda.synchronize()
+    for p, g in enumerate(gs):
+        g.check(f"{wl.name} {wl.proj_names[p]} N={N} ydt={ydt}")
+    return ys
+
+
+def run_layer(wl, layer, N, ydts, rows_per_proj=None, seed_rows=0):
+    """Build one layer on the GPU, run the driver once per output type,
+    compare every output with the oracle (all rows, or seeded samples)."""
+    if isinstance(ydts, int):
+        ydts = (ydts,)
+    print(f"{wl.name} layer {layer} N={N} ydts={ydts}", flush=True)
     ws = W.layer_weights(wl, layer, device="cpu" if wl.layers == 1 else DEV)
     packed_gpu = [bt.pack(w.to(DEV), s) for (w, s) in ws]
     L = bt.Layer(packed_gpu, wl.shapes)
     xs = W.layer_inputs(wl, layer, N, device="cpu")
-    ys = L.forward([x.to(DEV) for x in xs], y_dtype=ydt)
-    torch.cuda.synchronize()
+    xd = [x.to(DEV) for x in xs]
+    outs = {ydt: forward_guarded(L, wl, xd, N, ydt) for ydt in ydts}
     rng = np.random.default_rng(seed_rows)
     quant = [oracle.quant_act(x_for_oracle(x)) for x in xs]
     for p, ((w, s), (M, K)) in enumerate(zip(ws, wl.shapes)):
         ref_packed, _ = oracle.pack(w.cpu().numpy(), s)
         assert_equal(to_np(packed_gpu[p]), ref_packed, f"packed {wl.proj_names[p]}")
         xq, xsc, _ = quant[wl.proj_input[p]]
-        rows = None
-        if rows_per_proj is not None and rows_per_proj < M:
-            rows = np.sort(rng.choice(M, rows_per_proj, replace=False))
+        rows = sample_rows(rng, M, rows_per_proj)
         acc = oracle.matmul_i32(ref_packed, M, K, xq, rows)
-        check_projection(packed_gpu[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt,
-                         rows, f"{wl.name} layer {layer} {wl.proj_names[p]} N={N}")
-    return ys
+        for ydt, ys in outs.items():
+            check_projection(packed_gpu[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt,
+                             rows, f"{wl.name} layer {layer} {wl.proj_names[p]} N={N} ydt={ydt}")
+    return outs[ydts[0]]
 
 
 @pytest.mark.parametrize("N", SMALL.batches)
@@ -95,25 +120,34 @@ def test_workload_gemv_2560():
             assert_rel_close(as_f64(y), ref["y"], 1e-6, "y")
 
 
-@pytest.mark.parametrize("ydt", [bt.BT_I32, bt.BT_BF16])
-def test_workload_layer2b_n1(ydt):
-    run_layer(W.LAYER2B_N1, 0, 1, ydt)
+def test_workload_layer2b_n1():
+    run_layer(W.LAYER2B_N1, 0, 1, (bt.BT_I32, bt.BT_BF16, bt.BT_F32))
 
 
 def test_workload_layer2b_n64():
-    run_layer(W.LAYER2B_N64, 0, 64, bt.BT_BF16)
-    run_layer(W.LAYER2B_N64, 0, 64, bt.BT_I32, rows_per_proj=64)
+    run_layer(W.LAYER2B_N64, 0, 64, (bt.BT_I32, bt.BT_BF16, bt.BT_F32))
 
 
 def test_workload_prefill_sampled_rows():
-    run_layer(W.PREFILL2B_N2048, 0, 2048, bt.BT_BF16, rows_per_proj=48, seed_rows=1)
-    run_layer(W.PREFILL2B_N2048, 0, 2048, bt.BT_I32, rows_per_proj=24, seed_rows=2)
+    run_layer(W.PREFILL2B_N2048, 0, 2048, (bt.BT_I32, bt.BT_BF16), rows_per_proj=64,
+              seed_rows=1)
 
 
+# The 70B-class block: exact int32 sums on 256 sampled rows per projection
+# plus each projection's first and last row tile (the one-launch kernel at 1
+# token with its balanced two-class schedule, the matrix-core decode at 8,
+# and at 33 and 64 tokens where the down projection runs in K phases), and
+# the bf16 outputs of the same call.
 @pytest.mark.parametrize("layer", [0, 79])
 @pytest.mark.parametrize("N", [1, 8])
 def test_workload_stream70b_sampled_rows(layer, N):
-    run_layer(W.STREAM70B, layer, N, bt.BT_BF16, rows_per_proj=64, seed_rows=layer + N)
+    run_layer(W.STREAM70B, layer, N, (bt.BT_I32, bt.BT_BF16), rows_per_proj=256,
+              seed_rows=layer + N)
+
+
+@pytest.mark.parametrize("N", [33, 64])
+def test_workload_stream70b_many_tokens(N):
+    run_layer(W.STREAM70B, 0, N, (bt.BT_I32,), rows_per_proj=64, seed_rows=N)
 
 
 def test_determinism():
@@ -153,26 +187,28 @@ B3_BLOCK = W.Workload(
     weight_dist="p0_0.4", act_dist="normal", outlier_frac=0.005, outlier_scale=30.0)
 
 
-def run_layer_b3(wl, layer, N, ydt, rows_per_proj=None, seed_rows=0, per_group=False):
+def run_layer_b3(wl, layer, N, ydts, rows_per_proj=None, seed_rows=0, per_group=False):
     """The driver on base-3 weights against the oracle's product."""
+    if isinstance(ydts, int):
+        ydts = (ydts,)
+    print(f"base-3 {wl.name} layer {layer} N={N} ydts={ydts}", flush=True)
     ws = W.layer_weights(wl, layer, device="cpu" if wl.layers == 1 else DEV)
     packed = [bt.pack_b3(w.to(DEV), s) for (w, s) in ws]
     L = bt.Layer(packed, wl.shapes, base3=True)
     xs = W.layer_inputs(wl, layer, N, device="cpu")
-    ys = L.forward([x.to(DEV) for x in xs], y_dtype=ydt, per_group=per_group)
-    torch.cuda.synchronize()
+    xd = [x.to(DEV) for x in xs]
+    outs = {ydt: forward_guarded(L, wl, xd, N, ydt, per_group) for ydt in ydts}
     rng = np.random.default_rng(seed_rows)
     quant = [oracle.quant_act(x_for_oracle(x)) for x in xs]
     for p, ((w, s), (M, K)) in enumerate(zip(ws, wl.shapes)):
         ref_packed, _ = oracle.pack(w.cpu().numpy(), s)
         xq, xsc, _ = quant[wl.proj_input[p]]
-        rows = None
-        if rows_per_proj is not None and rows_per_proj < M:
-            rows = np.sort(rng.choice(M, rows_per_proj, replace=False))
+        rows = sample_rows(rng, M, rows_per_proj)
         acc = oracle.matmul_i32(ref_packed, M, K, xq, rows)
-        check_projection(packed[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt,
-                         rows, f"base-3 {wl.name} layer {layer} {wl.proj_names[p]} N={N}")
-    return ys
+        for ydt, ys in outs.items():
+            check_projection(packed[p], ref_packed, M, K, xq, xsc, acc, ys[p], ydt, rows,
+                             f"base-3 {wl.name} layer {layer} {wl.proj_names[p]} N={N} ydt={ydt}")
+    return outs[ydts[0]]
 
 
 @pytest.mark.parametrize("N", B3_BLOCK.batches)
@@ -221,6 +257,8 @@ def test_base3_layer_equals_two_bit_layer(N):
 
 @pytest.mark.parametrize("layer", [0, 79])
 def test_workload_stream70b_base3_sampled_rows(layer):
-    # the 70B-class block in base-3 bytes at one token: one launch
-    print(f"base-3 70B-class block, layer {layer}", flush=True)
-    run_layer_b3(W.STREAM70B, layer, 1, bt.BT_BF16, rows_per_proj=64, seed_rows=layer)
+    # the 70B-class block in base-3 bytes at one token (one launch): exact
+    # int32 sums on 256 sampled rows per projection plus its edge tiles, and
+    # the bf16 outputs
+    run_layer_b3(W.STREAM70B, layer, 1, (bt.BT_I32, bt.BT_BF16), rows_per_proj=256,
+                 seed_rows=layer)
