@@ -28,7 +28,8 @@
  *     no-op.
  *   - Every array argument is a DEVICE pointer, 16-byte aligned, owned by the
  *     caller.  The library never allocates, frees or synchronizes; scratch
- *     space is passed in by the caller (bt_layer_io.workspace).
+ *     space is passed in by the caller (bt_layer_io.workspace), except in
+ *     bt_layer_forward_noalloc, whose scratch is a static device array.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously on it; results are ready when the stream is.
  *   - Argument errors are returned synchronously as BT_ERR_* and nothing is
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 6
+#define BT_ABI_VERSION 7
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -366,6 +367,33 @@ size_t bt_layer_workspace_bytes(const bt_layer *layer, int64_t N);
 
 bt_status bt_layer_forward(const bt_layer *layer, const bt_layer_io *io,
                            bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Allocation-free per-layer driver.  For callers that cannot allocate device
+ * memory or hand in a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.
+ *
+ * bt_layer_forward_noalloc runs exactly what bt_layer_forward runs for the
+ * same layer and io, with identical results; io->workspace and
+ * io->workspace_bytes are ignored.  The scratch those kernels use (the
+ * quantized inputs, their scales and sums: bt_layer_workspace_bytes(layer,
+ * io->N) bytes) is a static device array of BT_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends (32 MiB:
+ * e.g. 2048 tokens of a 2560/6912 block need 29.9 MB, 8 tokens of an
+ * 8192/28672 block 0.43 MB, 1..4 tokens of a one-launch block none).
+ *   - A call that needs more returns BT_ERR_WORKSPACE and launches nothing;
+ *     every other argument error is reported as by bt_layer_forward.
+ *   - Nothing is allocated, freed or synchronized.  The first call on a GPU
+ *     looks up the array's address there (hipGetSymbolAddress); later calls
+ *     reuse it.
+ *   - Every call on one GPU uses that GPU's array.  Calls ordered on one
+ *     stream are safe; calls that overlap on one GPU (other streams, other
+ *     host threads without ordering) race and their results are undefined.
+ * ---------------------------------------------------------------------- */
+#define BT_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+bt_status bt_layer_forward_noalloc(const bt_layer *layer, const bt_layer_io *io,
+                                   bt_stream stream);
 
 /* 1 if bt_layer_forward runs this layer of T16Q256 weights for N tokens of
  * x_dtype as one launch (io->flags 0), 0 if as per-group launches, -1 if the

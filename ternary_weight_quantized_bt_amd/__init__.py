@@ -84,7 +84,7 @@ BT_WSCALE_ABSMAX = 1
 BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 
@@ -150,6 +150,9 @@ def lib() -> ctypes.CDLL:
         L.bt_layer_forward.argtypes = [ctypes.POINTER(bt_layer),
                                        ctypes.POINTER(bt_layer_io), P]
         L.bt_layer_forward.restype = S
+        L.bt_layer_forward_noalloc.argtypes = [ctypes.POINTER(bt_layer),
+                                               ctypes.POINTER(bt_layer_io), P]
+        L.bt_layer_forward_noalloc.restype = S
         _lib = L
     return _lib
 
@@ -318,6 +321,14 @@ def bt_layer_workspace_bytes(layer: bt_layer, N: int) -> int:
 def bt_layer_forward(layer: bt_layer, io: bt_layer_io, stream=None):
     _check(lib().bt_layer_forward(ctypes.byref(layer), ctypes.byref(io),
                                   _stream(stream)))
+
+
+BT_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def bt_layer_forward_noalloc(layer: bt_layer, io: bt_layer_io, stream=None):
+    _check(lib().bt_layer_forward_noalloc(ctypes.byref(layer), ctypes.byref(io),
+                                          _stream(stream)))
 
 
 # -------------------------------------------------------------- helpers ----

@@ -374,8 +374,12 @@ size_t bt_layer_workspace_bytes(const bt_layer *L, int64_t N) {
     return carve(Kin, N, nullptr).bytes;
 }
 
-bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream stream) {
-    const char *fn = "bt_layer_forward";
+}  // extern "C"
+
+namespace bt {
+
+bt_status layer_check(const bt_layer *L, const bt_layer_io *io, const char *fn,
+                      size_t *scratch_bytes) {
     if (L == nullptr || io == nullptr)
         return fail(BT_ERR_INVALID_ARG, "%s: layer or io is NULL", fn);
     int64_t Kin[BT_LAYER_INPUTS];
@@ -394,14 +398,28 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)io->y_dtype);
     if (io->flags & ~(BT_LAYER_PER_GROUP | BT_LAYER_BASE3))
         return fail(BT_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, (unsigned)io->flags);
+    *scratch_bytes = 0;
     if (N == 0) return ok();
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) BT_TRY(check_ptr(io->x[i], "io->x[i]", fn));
     for (int p = 0; p < BT_LAYER_PROJ; ++p) BT_TRY(check_ptr(io->y[p], "io->y[p]", fn));
+    *scratch_bytes = carve(Kin, N, nullptr).bytes;
+    return ok();
+}
+
+bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspace,
+                        size_t workspace_bytes, bt_stream stream, const char *fn) {
+    size_t need_bytes = 0;
+    BT_TRY(layer_check(L, io, fn, &need_bytes));
+    const int64_t N = io->N;
+    if (N == 0) return ok();
+    int64_t Kin[BT_LAYER_INPUTS];
+    layer_input_widths(L, Kin);
+    const bool base3 = (io->flags & BT_LAYER_BASE3) != 0;
     const LayerWs need = carve(Kin, N, nullptr);
-    if (io->workspace == nullptr || io->workspace_bytes < need.bytes)
+    if (workspace == nullptr || workspace_bytes < need.bytes)
         return fail(BT_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need.bytes,
-                    io->workspace == nullptr ? (size_t)0 : io->workspace_bytes);
-    if (reinterpret_cast<uintptr_t>(io->workspace) & 255u)
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(BT_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
 
     hipStream_t s = as_stream(stream);
@@ -415,7 +433,7 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         }
         // the inputs quantized into the workspace (one launch, or one per
         // group before its products), then one base-3 product per projection
-        const LayerWs ws = carve(Kin, N, io->workspace);
+        const LayerWs ws = carve(Kin, N, workspace);
         if (!per_group) {
             bt::QuantJobs jobs{};
             for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
@@ -449,7 +467,7 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         const hipError_t e = bt::launch_layer(la, io->x_dtype, s);
         return e == hipSuccess ? ok() : hip_status(e, fn);
     }
-    const LayerWs ws = carve(Kin, N, io->workspace);
+    const LayerWs ws = carve(Kin, N, workspace);
     const bool per_group = (io->flags & BT_LAYER_PER_GROUP) != 0;
     // The four inputs are all valid at the call: unless asked for per-group
     // launches, the ones that need codes in the workspace are quantized in
@@ -512,6 +530,18 @@ bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream s
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return ok();
+}
+
+bt_status fail_with(bt_status st, const char *msg) { return fail(st, "%s", msg); }
+
+}  // namespace bt
+
+extern "C" {
+
+bt_status bt_layer_forward(const bt_layer *L, const bt_layer_io *io, bt_stream stream) {
+    if (io == nullptr) return fail(BT_ERR_INVALID_ARG, "bt_layer_forward: layer or io is NULL");
+    return bt::layer_forward(L, io, io->workspace, io->workspace_bytes, stream,
+                             "bt_layer_forward");
 }
 
 int bt_layer_one_launch(const bt_layer *L, int64_t N, bt_dtype x_dtype) {

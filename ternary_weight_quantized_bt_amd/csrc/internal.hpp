@@ -87,4 +87,15 @@ int device_cus();
 // Largest N for which launch_decode uses the dot4 kernel.
 constexpr int64_t kDot4MaxN = 4;
 
+// The per-layer driver behind bt_layer_forward with its scratch passed
+// explicitly (`fn` names the entry point in error messages), and its argument
+// checks alone: every check but the workspace's, and the scratch bytes the
+// call needs (0 when it launches nothing).  Host only; no GPU call.
+bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspace,
+                        size_t workspace_bytes, bt_stream stream, const char *fn);
+bt_status layer_check(const bt_layer *L, const bt_layer_io *io, const char *fn,
+                      size_t *scratch_bytes);
+// Records `msg` as the calling thread's last error and returns st.
+bt_status fail_with(bt_status st, const char *msg);
+
 }  // namespace bt

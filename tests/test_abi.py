@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
               "bt_b3_bytes", "bt_pack_ternary_b3", "bt_unpack_ternary_b3",
               "bt_ternary_gemv_b3",
               "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
-              "bt_layer_workspace_bytes", "bt_packed_bytes", "bt_last_error",
+              "bt_layer_workspace_bytes", "bt_layer_forward_noalloc",
+              "bt_packed_bytes", "bt_last_error",
               "bt_abi_version"):
         assert n in names
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 6
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 7
 
 
 def test_packed_bytes():
@@ -283,3 +284,39 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         bt.bt_ternary_gemv(torch.zeros(16), 16, 256, None, None, None, 0, None,
                            bt.BT_F32, stream=0)
+
+
+def test_layer_noalloc_validation_on_the_host():
+    """The allocation-free driver reports argument errors and scratch beyond
+    its static array before it touches a device (nothing here launches)."""
+    big = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192),
+           (28672, 8192), (8192, 28672)]
+    L = _layer(big)
+    io = bt.bt_layer_io()
+    for i in range(4):
+        io.x[i] = A
+    for p in range(7):
+        io.y[p] = A
+    io.x_dtype = bt.BT_BF16
+    io.y_dtype = bt.BT_I32
+    # 640 tokens of this block need 34 MB of scratch: refused
+    io.N = 640
+    assert bt.bt_layer_workspace_bytes(L, 640) > bt.BT_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward_noalloc(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_WORKSPACE
+    assert "static scratch" in bt.bt_last_error()
+    # other argument errors are the workspace driver's
+    io.N = 8
+    io.y_dtype = 9
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward_noalloc(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_DTYPE
+    io.y_dtype = bt.BT_I32
+    io.x[2] = None
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_layer_forward_noalloc(L, io, stream=0)
+    assert e.value.status == bt.BT_ERR_INVALID_ARG
+    io.N = 0  # nothing to do, no device touched
+    bt.bt_layer_forward_noalloc(L, io, stream=0)
+    assert bt.BT_NOALLOC_SCRATCH_BYTES == 32 << 20
