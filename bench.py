@@ -38,6 +38,7 @@ METRIC = ("packed-weight GB/s & % HBM peak (decode GEMV); "
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix cores, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace.json")
 # Sources of each measured kernel: a traffic record is only used while they
 # are unchanged since the counters were taken.
 KERNEL_SOURCES = {
@@ -75,12 +76,23 @@ def parse():
     ap.add_argument("--base3-only", action="store_true",
                     help="only compare the 2-bit and base-3 weight formats on the "
                          "70B-class matrices (--layers blocks deep, default 8)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="no GPU: read the rocprofv3 --kernel-trace csv output of a "
+                         "default-workload bench run made with the same --steps / "
+                         "--warmup / --layers, keep the per-layer kernel's dispatches "
+                         "of the timed steps only, and rewrite its entry of "
+                         "profiles/kernel_trace.json")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR",
                     help="no GPU: read four rocprofv3 --pmc output folders (copy "
                          "FETCH_SIZE, copy WRITE_SIZE, step FETCH_SIZE, step "
                          "WRITE_SIZE) and rewrite the layer kernel's entry of "
                          "profiles/traffic.json")
     return ap.parse_args()
+
+
+def note(msg: str):
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_sha(kernel_name: str) -> str:
@@ -296,77 +308,198 @@ def traffic_summary(copy_fetch, copy_write, k_fetch, k_write):
     print(json.dumps(entry, indent=1))
 
 
+def _trace_rows(folder):
+    """(kernel name, start ns, end ns) of every dispatch in a rocprofv3
+    --kernel-trace csv output folder, in start order."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]),
+                             int(r["End_Timestamp"])))
+    rows.sort(key=lambda r: r[1])
+    return rows
+
+
+def _headline_kernel(name):
+    """The one-token per-layer kernel on T16Q256 weights (template arguments
+    <element type, tokens, waves, K split, ring, base-3>)."""
+    if "layer_dot4_kernel<" not in name:
+        return False
+    args = [a.strip() for a in name.split("layer_dot4_kernel<", 1)[1].split(">", 1)[0].split(",")]
+    return len(args) == 6 and args[1] == "1" and args[5] == "false"
+
+
+def trace_summary(folder, steps, warmup, layers, out=TRACE_FILE):
+    """Durations of the per-layer kernel's dispatches inside the timed window
+    of a bench run: the run's first `layers` dispatches of it are the eager
+    step before the graph capture, the next warmup * layers the untimed graph
+    replays, the next steps * layers the timed replays."""
+    import statistics
+    name = "layer_dot4_kernel"
+    rows = [r for r in _trace_rows(folder) if _headline_kernel(r[0])]
+    skip, count = layers * (1 + warmup), layers * steps
+    if len(rows) < skip + count:
+        raise SystemExit(f"{len(rows)} dispatches of the kernel, need {skip + count}")
+    win = rows[skip:skip + count]
+    d = [(e - b) / 1e3 for _, b, e in win]
+    span = (win[-1][2] - win[0][1]) / 1e3
+    entry = {
+        "kernel_sha": kernel_sha(name),
+        "kernel_instance": win[0][0],
+        "timed_dispatches": count,
+        "mean_us": round(statistics.fmean(d), 3),
+        "median_us": round(statistics.median(d), 3),
+        "min_us": round(min(d), 3),
+        "max_us": round(max(d), 3),
+        "window_span_ms": round(span / 1e3, 4),
+        "span_per_step_ms": round(span / steps / 1e3, 4),
+        "busy_fraction_of_span": round(sum(d) / span, 4),
+        "steps": steps, "warmup": warmup, "layers": layers,
+        "skipped_dispatches": skip,
+    }
+    try:
+        with open(out) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        doc = {}
+    doc[name] = entry
+    with open(out, "w") as f:
+        json.dump(doc, f, indent=1)
+    print(json.dumps(entry, indent=1))
+    return entry
+
+
+def read_trace(kernel_name, sha):
+    try:
+        with open(TRACE_FILE) as f:
+            e = json.load(f).get(kernel_name)
+    except (OSError, ValueError):
+        return None
+    return e if e and e.get("kernel_sha") == sha else None
+
+
 def _block_packed_bytes():
     """Packed code bytes of one 70B-class block (the seven projections)."""
     import workloads as W
     return W.STREAM70B.packed_bytes_per_layer
 
 
-def cpu_baseline(wl, N, budget_s):
-    """The oracle on layer 0 of the workload (all seven projections, the same
-    seeded weights and inputs), repeated until the time budget is used."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def _repeat(fn, budget_s):
+    """Calls fn until budget_s have passed (at least once): (calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return reps, el
+
+
+def _oracle_layer(wl, N, rows_per_proj=None):
+    """The oracle's whole path on layer 0 of a workload (the same seeded
+    weights and inputs as the GPU): per projection, quantize its input, the
+    exact product (all rows, or a fixed sample of rows), dequantization.
+    Returns (callable, packed bytes it streams, int8 ops it performs)."""
     import numpy as np
     import torch
     import oracle
     import workloads as W
     dev = "cuda:0"
-    packed = []
+    packed, rows = [], []
     for p, (M, K) in enumerate(wl.shapes):
         w = W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, 0, p), dev).cpu().numpy()
         packed.append(oracle.pack(w, W.weight_scale(wl, p))[0])
         del w
+        rows.append(None if rows_per_proj is None else
+                    np.linspace(0, M - 1, rows_per_proj).astype(np.int64))
     xs = W.layer_inputs(wl, 0, N, dev)
     xs = [x.cpu().view(torch.uint16).numpy() if x.dtype == torch.bfloat16
           else x.cpu().numpy() for x in xs]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def run():
         for p, (M, K) in enumerate(wl.shapes):
-            oracle.forward(packed[p], M, K, xs[wl.proj_input[p]])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    cores = min(cores, len(os.sched_getaffinity(0)))
-    # the same oracle on one thread (OpenMP's thread count of this thread;
-    # the results do not depend on it), on a shorter sample
-    one = None
+            xq, xsc, _ = oracle.quant_act(xs[wl.proj_input[p]])
+            acc = oracle.matmul_i32(packed[p], M, K, xq, rows[p])
+            oracle.dequant(acc, oracle.scale_of(packed[p], M, K), xsc)
+    nrow = [M if r is None else len(r) for (M, _), r in zip(wl.shapes, rows)]
+    streamed = sum(n * K // 4 for n, (_, K) in zip(nrow, wl.shapes))
+    ops = 2 * N * sum(n * K for n, (_, K) in zip(nrow, wl.shapes))
+    return run, streamed, ops
+
+
+def _threads(n):
+    """Sets the oracle's OpenMP thread count (its results do not depend on
+    it); returns False if the runtime cannot be reached."""
     try:
         import ctypes
-        gomp = ctypes.CDLL("libgomp.so.1")
-        gomp.omp_set_num_threads(1)
-        reps1, t1 = 0, time.perf_counter()
-        while True:
-            for p, (M, K) in enumerate(wl.shapes):
-                oracle.forward(packed[p], M, K, xs[wl.proj_input[p]])
-            reps1 += 1
-            el1 = time.perf_counter() - t1
-            if el1 >= budget_s / 4:
-                break
-        gomp.omp_set_num_threads(cores)
-        one = round(wl.packed_bytes_per_layer * reps1 / el1 / 1e9, 4)
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(n)
+        return True
     except OSError:
-        pass
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+        return False
+
+
+def cpu_baseline(wl, N, budget_s):
+    """The oracle on layer 0 of the benchmarked workload (all seven
+    projections, the same seeded weights and inputs), repeated until the time
+    budget is used, on the host's threads and then on one thread; and the
+    same for the four smaller workloads (single GEMV, 2B-style block at 1 and
+    64 tokens, the 2048-token prefill on a fixed sample of output rows)."""
+    import oracle
+    import workloads as W
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    cores = min(cores, len(os.sched_getaffinity(0)))
+    run, streamed, _ = _oracle_layer(wl, N)
+    reps, el = _repeat(run, budget_s)
+    one = None
+    if _threads(1):
+        reps1, el1 = _repeat(run, budget_s / 4)
+        _threads(cores)
+        one = round(streamed * reps1 / el1 / 1e9, 4)
+    per_config = {}
+    for cwl, cN, rows, label in (
+            (W.GEMV_2560, 1, None, "quantization + product + dequantization, all rows"),
+            (W.LAYER2B_N1, 1, None, "7 projections, all rows"),
+            (W.LAYER2B_N64, 64, None, "7 projections, all rows"),
+            (W.PREFILL2B_N2048, 2048, 32,
+             "7 projections, all 2048 tokens quantized, products on 32 evenly spaced "
+             "rows per projection")):
+        crun, cbytes, cops = _oracle_layer(cwl, cN, rows)
+        entry = {"tokens": cN, "sample": label}
+        for name, threads, budget in (("threads", cores, 2.0), ("one_thread", 1, 1.0)):
+            if threads == 1 and not _threads(1):
+                continue
+            r, t = _repeat(crun, budget)
+            entry[name] = {"calls": r, "seconds": round(t, 2),
+                           "ms_per_call": round(t / r * 1e3, 3),
+                           "packed_gb_per_s": round(cbytes * r / t / 1e9, 4),
+                           "int8_tops": round(cops * r / t / 1e12, 6)}
+        _threads(cores)
+        per_config[cwl.name] = entry
     return {
-        "value": round(wl.packed_bytes_per_layer * reps / el / 1e9, 4),
+        "value": round(streamed * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
         "sample": f"layer 0 of {wl.name} (all 7 projections, {N} token(s)), "
                   f"{reps} pass(es) in {el:.1f} s",
         "one_thread_value": one,
-        "cpu_model": cpu_model,
+        "cpu_model": _cpu_model(),
         "compile_flags": " ".join(oracle.CFLAGS),
+        "per_config": per_config,
     }
 
 
@@ -602,6 +735,11 @@ def main():
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
+    if args.trace_summary:
+        import workloads as W
+        trace_summary(args.trace_summary, args.steps, args.warmup,
+                      args.layers or W.BY_NAME[args.workload].layers)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the library has no multi-GPU path", file=sys.stderr)
@@ -642,6 +780,7 @@ def main():
           file=sys.stderr, flush=True)
 
     sec, wall = run_steps(model, args.steps, args.warmup, use_graph)
+    note(f"timed steps done: {sec * 1e3:.4f} ms per step")
     eager_sec = None
     if use_graph:
         eager_sec, _ = run_steps(model, max(3, args.steps // 4), 2, False)
@@ -688,6 +827,14 @@ def main():
     roofline["traffic"] = read_traffic(kernel_name, kernel_sha(kernel_name))
     roofline["kernel"] = kernel_name
     roofline["kernel_avg_us"] = round(kavg * 1e6, 3)
+    # The same kernel's mean duration in a rocprofv3 kernel trace of this
+    # command (timed dispatches only), while its sources are unchanged: it
+    # excludes the gaps between launches that the event figure includes.
+    tr = read_trace(kernel_name, kernel_sha(kernel_name)) if decode else None
+    if tr:
+        roofline["rocprof_kernel_avg_us"] = tr["mean_us"]
+        roofline["rocprof_frac"] = round(bytes_per_launch / (tr["mean_us"] * 1e-6) / 1e9
+                                         / PEAK_HBM_GBS, 4)
     roofline["launches_per_step"] = launches_per_step
     roofline["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
     roofline["prequantized_group_kernel_avg_us"] = round(kt * 1e6, 3)
@@ -717,15 +864,21 @@ def main():
     if not args.no_extra:
         del model
         torch.cuda.empty_cache()
+        note("extra: 2048-token prefill")
         extra["prefill2b_n2048"] = prefill_extra(args.steps, args.warmup, use_graph)
+        note("extra: weight quantizer")
         extra["weight_quantizer_70b_gate"] = weight_quant_extra(args.steps, args.warmup)
+        note("extra: base-3 against 2-bit matrices")
         extra["base3_vs_2bit_70b"] = base3_extra(args.steps, args.warmup, use_graph)
         if wl.name == "stream70b" and N == 1:
+            note("extra: base-3 stream")
             extra["stream70b_1_token_base3"] = base3_stream_extra(wl, layers, args.steps,
                                                                   args.warmup, use_graph,
                                                                   value, sec)
+        note("extra: small configurations")
         extra["small_configs_hot_and_cold"] = small_configs_extra(args.steps, args.warmup,
                                                                   use_graph)
+        note("extra: device copies")
         copy = copy_bandwidth_extra()
         extra["device_copy_gb_per_s_read_plus_write"] = copy
         # copies of 1 GB and more run from HBM (smaller ones from the caches)
@@ -734,6 +887,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
+        note("oracle on the host")
         cpu = cpu_baseline(wl, N, args.cpu_seconds)
 
     out = {
