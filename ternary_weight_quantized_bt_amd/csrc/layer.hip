@@ -152,91 +152,6 @@ void layer_dot4_kernel(LayerArgs a) {
     const int h = lane / 16;
     const int nvalid = (int)min((int64_t)NT, a.N);
     const int kpart = wave % P, sub = wave / P;
-    // Tile bookkeeping in 32-bit scalars: tile and slot counts are far below
-    // 2^31, and 64-bit compares would run on the vector unit.
-    const int total = a.tend32[kLayerProj - 1];
-    const int ngroups = (total + TPW - 1) / TPW;
-    // This workgroup's tile groups (see LayerArgs::sched): nS light ones from
-    // sfirst, then nB heavy ones from bfirst; or every G-th from w.
-    const int G = (int)gridDim.x, w = (int)blockIdx.x;
-    int nS = 0, sfirst = 0, nB = 0, bfirst = 0;
-    if (a.sched) {
-        const int c = w < a.n0 ? 0 : 1;
-        const int i = c ? w - a.n0 : w, nc = c ? G - a.n0 : a.n0;
-        const int ss = c ? a.sstart[1] : a.sstart[0], sc = c ? a.scount[1] : a.scount[0];
-        sfirst = ss + (int)((int64_t)i * sc / nc);
-        nS = ss + (int)((int64_t)(i + 1) * sc / nc) - sfirst;
-        nB = c ? a.heavy[1] : a.heavy[0];
-        bfirst = a.ts + (c ? a.n0 * a.heavy[0] : 0) + i * nB;
-    }
-    const int nit = a.sched ? nS + nB : (ngroups - w + G - 1) / G;
-    auto group_of = [&](int it) {
-        return a.sched ? (it < nS ? sfirst + it : bfirst + (it - nS)) : w + it * G;
-    };
-    auto tile_of = [&](int it) { return group_of(it) * TPW + sub; };
-    // This wave's blocks in a tile of input group g: kpart, kpart + P, ...
-    // (interleaved, so the waves of a tile read neighbouring KiB together),
-    // nq(g) of them, at least one (K >= 256 * P).
-    auto nq = [&](int g) { return (sel(a.qb32, g) - kpart + P - 1) / P; };
-    // Projection of a tile index that only grows (each cursor below walks
-    // its tiles in order): re-resolved only when the tile leaves the current
-    // projection's tile range [start, end).
-    struct Win {
-        int p, start, end;
-    };
-    auto win0 = [&]() { return Win{0, 0, a.tend32[0]}; };
-    auto seek = [&](Win &w, int t) {
-        while (t >= w.end) {
-            ++w.p;
-            w.start = w.end;
-            w.end = sel(a.tend32, w.p);
-        }
-    };
-
-    // Slots of this wave: nq(g) per tile of input group g among its tiles.
-    int nslots = 0;
-    if (a.sched) {
-        // tiles tg*TPW + sub for tile groups tg in [g0, g1), per input group
-        auto count = [&](int g0, int g1) {
-            int n = 0, prev = 0;
-#pragma unroll
-            for (int g = 0; g < kLayerInputs; ++g) {
-                const int end = a.gend32[g];
-                const int lo = max(g0, (prev - sub + TPW - 1) / TPW);
-                const int hi = min(g1, (end - sub + TPW - 1) / TPW);
-                n += hi > lo ? (hi - lo) * nq(g) : 0;
-                prev = end;
-            }
-            return n;
-        };
-        nslots = count(sfirst, sfirst + nS) + count(bfirst, bfirst + nB);
-    } else {
-        // the sequence o + it*S (it >= 0) inside each group's tile range
-        const int o = w * TPW + sub, S = G * TPW;
-        auto upto = [&](int x) { return x <= o ? 0 : (x - o + S - 1) / S; };
-        int prev = 0;
-#pragma unroll
-        for (int g = 0; g < kLayerInputs; ++g) {
-            const int end = a.gend32[g];
-            nslots += (upto(end) - upto(prev)) * nq(g);
-            prev = end;
-        }
-    }
-    const bool has_work = nit > 0 && tile_of(0) < total;
-
-    // Weight scales, one per projection in its packed tail: lane p < 7 of
-    // wave 0 loads scale p.  A divergent address makes it a vector load,
-    // issued first and waited for only where the scales are written to LDS at
-    // the end of the prologue: a scalar load of these cold lines would share
-    // the counter that the prologue's barriers wait on for LDS, and every
-    // workgroup would sit out an HBM round trip before quantizing.
-    const int sp = min(lane, kLayerProj - 1);
-    const int64_t code_bytes = B3 ? b3_code_bytes(sel(a.M, sp), sel(a.K, proj_group(sp)))
-                                  : sel(a.M, sp) * sel(a.K, proj_group(sp)) / 4;
-    float wsl = 0.0f;
-    if (wave == 0)
-        wsl = *to_global(reinterpret_cast<const float *>(sel(a.packed, sp) + code_bytes));
-
     // ---- prologue, part 1: this wave's input chunks into registers ----
     // Wave w owns chunks [w * kSpan, (w + 1) * kSpan) of the sequence; lane l
     // holds chunks w * kSpan + 64c + l (c < kLayerUnits), so every load is one
@@ -315,11 +230,45 @@ void layer_dot4_kernel(LayerArgs a) {
         s_sum[threadIdx.x] = 0;
     }
 
+    // Tile bookkeeping in 32-bit scalars: tile and slot counts are far below
+    // 2^31, and 64-bit compares would run on the vector unit.
+    const int total = a.tend32[kLayerProj - 1];
+    // This workgroup's tile groups (see LayerArgs::sched and LayerSched): nS
+    // light ones from sfirst, then nB heavy ones from bfirst; or every G-th
+    // from w.
+    const int G = (int)gridDim.x, w = (int)blockIdx.x;
+    const LayerSched ls(a, w, G, TPW);
+    const int nit = ls.nit;
+    auto group_of = [&](int it) { return ls.group_of(it); };
+    auto tile_of = [&](int it) { return group_of(it) * TPW + sub; };
+    // This wave's blocks in a tile of input group g: kpart, kpart + P, ...
+    // (interleaved, so the waves of a tile read neighbouring KiB together),
+    // nq(g) of them, at least one (K >= 256 * P).
+    auto nq = [&](int g) { return (sel(a.qb32, g) - kpart + P - 1) / P; };
+    // Projection of a tile index that only grows (each cursor below walks
+    // its tiles in order): re-resolved only when the tile leaves the current
+    // projection's tile range [start, end).
+    struct Win {
+        int p, start, end;
+    };
+    auto win0 = [&]() { return Win{0, 0, a.tend32[0]}; };
+    auto seek = [&](Win &w, int t) {
+        while (t >= w.end) {
+            ++w.p;
+            w.start = w.end;
+            w.end = sel(a.tend32, w.p);
+        }
+    };
+
+    // Slots of this wave: nq(g) per tile of input group g among its tiles.
+    const int nslots = ls.slots(a, sub, kpart, P);
+    const bool has_work = nit > 0 && tile_of(0) < total;
+
     // Load cursor: tile iteration lit, lrem slots left in its tile (the
     // current one included), lleft slots left to load.  On the last slot it
     // stays put, so every ring load is unconditional (a harmless reload).
     int lit = 0, lrem = 0, lleft = nslots;
-    gptr<const v4u> lp;        // T16Q256: this lane's 16 bytes of the slot
+    const uint8_t *lp = nullptr;  // T16Q256: the slot (wave-uniform)
     const uint8_t *lt = nullptr;  // B3T1024: the tile
     Win lw = win0();
     int lnq = 0, lqb = 0;
@@ -336,8 +285,7 @@ void layer_dot4_kernel(LayerArgs a) {
         if constexpr (B3)
             lt = lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kB3TileBytes;
         else
-            lp = to_global(reinterpret_cast<const v4u *>(
-                     lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kTileBytes)) + lane;
+            lp = lbase + ((int64_t)(t - lw.start) * lqb + kpart) * kTileBytes;
     };
     point(has_work ? tile_of(0) : 0);
     auto advance_load = [&]() {
@@ -347,7 +295,7 @@ void layer_dot4_kernel(LayerArgs a) {
             if constexpr (B3)
                 lt += (int64_t)kB3TileBytes * P;
             else
-                lp += kWave * P;
+                lp += (int64_t)kTileBytes * P;
             return;
         }
         point(tile_of(++lit));
@@ -357,7 +305,7 @@ void layer_dot4_kernel(LayerArgs a) {
         if constexpr (B3)
             return load_slot<true>(lt, lane);
         else
-            return __builtin_nontemporal_load(lp);
+            return __builtin_nontemporal_load(to_global(reinterpret_cast<const v4u *>(lp)) + lane);
     };
     constexpr int kSlots = RING + 1;
     Slot ring[kSlots];
@@ -401,7 +349,28 @@ void layer_dot4_kernel(LayerArgs a) {
             }
         }
     }
+    // every input chunk has landed (absmax read them all): say so, so that
+    // the quantization below needs no wait that would also cover the scale
+    // and ring loads issued next
+    if constexpr (!B3) __builtin_amdgcn_s_waitcnt(0x3F70);
     __syncthreads();
+    // Weight scales, one per projection in its packed tail (addresses made
+    // on the host): lane p < 7 of wave 0 loads scale p, after the input
+    // loads, and it is waited for only where the scales go to LDS at the end
+    // of the prologue.  The seven addresses are opaque scalars picked per
+    // lane, so no indexed load of the argument block sits in front of it.
+    float wsl = 0.0f;
+    if (wave == 0) {
+        const float *sp = a.wscale[0];
+#pragma unroll
+        for (int k = 1; k < kLayerProj; ++k) {
+            const float *q = a.wscale[k];
+            asm volatile("" : "+s"(q));
+            sp = lane == k ? q : sp;
+        }
+        wsl = *to_global(sp);
+    }
+
     // The first 2-bit weight slots go out here, behind the input loads: issued
     // before the first barrier they queue with the input loads and hold up
     // every wave's arrival there (the vector-memory queue is full at that
@@ -682,12 +651,19 @@ hipError_t launch_layer_t(const LayerArgs &args, size_t lds, hipStream_t s) {
     const int64_t groups = (args.tend[kLayerProj - 1] + TPW - 1) / TPW;
     const int64_t grid = min(groups, (int64_t)device_cus());
     LayerArgs a = args;
-    plan_schedule<TPW>(a, (int)grid, B3 ? kIterCostB3 : kIterCostBlocks);
+    plan_layer_schedule(a, (int)grid, B3);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kLayerThreads), lds, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+void plan_layer_schedule(LayerArgs &a, int G, bool b3) {
+    if (b3)
+        plan_schedule<kLayerWaves / kLayerSplitB3>(a, G, kIterCostB3);
+    else
+        plan_schedule<kLayerWaves / kLayerSplit>(a, G, kIterCostBlocks);
+}
 
 bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
                    bt_dtype xdt, bool b3) {
@@ -747,6 +723,11 @@ LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kL
     a.ydt = (int)ydt;
     a.b3 = b3 ? 1 : 0;
     a.tab32 = (int)((xo + 15) / 16 * 16);  // base-3 table after the codes
+    for (int p = 0; p < kLayerProj; ++p) {
+        const int64_t Kp = a.K[proj_group(p)];
+        a.wscale[p] = reinterpret_cast<const float *>(
+            w[p] + (b3 ? b3_code_bytes(M[p], Kp) : M[p] * Kp / 4));
+    }
     return a;
 }
 

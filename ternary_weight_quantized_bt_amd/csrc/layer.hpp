@@ -41,7 +41,88 @@ struct LayerArgs {
     // Weight format: 0 = T16Q256; 1 = base-3 B3T1024 (qb32 then counts
     // 1024-column tile columns, and the decode table sits at LDS byte tab32).
     int b3, tab32;
+    const float *wscale[kLayerProj];  // each projection's weight scale (packed tail)
 };
+
+// One workgroup's work under a LayerArgs schedule, shared by the kernel and
+// the host-side schedule tests (so they check exactly what the kernel runs):
+// nit iterations; in iteration it, sub-group s (of tpw) takes the row tile
+// tile_for(it, s) (nothing if it is past the last tile), its waves splitting
+// the tile's K blocks.
+struct LayerSched {
+    int nS, sfirst, nB, bfirst, nit, w, G, sched, tpw;
+
+    __host__ __device__ LayerSched(const LayerArgs &a, int w_, int G_, int tpw_)
+        : nS(0), sfirst(0), nB(0), bfirst(0), nit(0), w(w_), G(G_), sched(a.sched), tpw(tpw_) {
+        if (sched) {
+            // nS light tile groups from sfirst, then nB heavy ones from bfirst
+            const int c = w < a.n0 ? 0 : 1;
+            const int i = c ? w - a.n0 : w, nc = c ? G - a.n0 : a.n0;
+            const int ss = c ? a.sstart[1] : a.sstart[0], sc = c ? a.scount[1] : a.scount[0];
+            sfirst = ss + (int)((int64_t)i * sc / nc);
+            nS = ss + (int)((int64_t)(i + 1) * sc / nc) - sfirst;
+            nB = c ? a.heavy[1] : a.heavy[0];
+            bfirst = a.ts + (c ? a.n0 * a.heavy[0] : 0) + i * nB;
+            nit = nS + nB;
+        } else {
+            // every G-th tile group from w
+            const int ngroups = (a.tend32[kLayerProj - 1] + tpw - 1) / tpw;
+            nit = (ngroups - w + G - 1) / G;
+        }
+    }
+    __host__ __device__ int group_of(int it) const {
+        return sched ? (it < nS ? sfirst + it : bfirst + (it - nS)) : w + it * G;
+    }
+    __host__ __device__ int tile_for(int it, int s) const { return group_of(it) * tpw + s; }
+    // K blocks of a tile of input group g (256-column blocks, or 1024-column
+    // base-3 tile columns), and a wave's share kp, kp + P, ... of them.
+    __host__ __device__ static int blocks(const LayerArgs &a, int g) {
+        int q = a.qb32[0];
+#pragma unroll
+        for (int k = 1; k < kLayerInputs; ++k) q = g == k ? a.qb32[k] : q;
+        return q;
+    }
+    __host__ __device__ static int nq(const LayerArgs &a, int g, int kp, int P) {
+        return (blocks(a, g) - kp + P - 1) / P;
+    }
+    // Slots (blocks) that the wave with K part kpart of sub-group sub streams
+    // over all its iterations, per input group in closed form.
+    __host__ __device__ int slots(const LayerArgs &a, int sub, int kpart, int P) const {
+        int n = 0;
+        if (sched) {
+            // tiles tg * tpw + sub for tile groups tg in [g0, g1), per input group
+            auto count = [&](int g0, int g1) {
+                int c = 0, prev = 0;
+#pragma unroll
+                for (int g = 0; g < kLayerInputs; ++g) {
+                    const int end = a.gend32[g];
+                    const int l0 = (prev - sub + tpw - 1) / tpw, h0 = (end - sub + tpw - 1) / tpw;
+                    const int lo = g0 > l0 ? g0 : l0, hi = g1 < h0 ? g1 : h0;
+                    c += hi > lo ? (hi - lo) * nq(a, g, kpart, P) : 0;
+                    prev = end;
+                }
+                return c;
+            };
+            n = count(sfirst, sfirst + nS) + count(bfirst, bfirst + nB);
+        } else {
+            // the sequence o + it*S (it >= 0) inside each group's tile range
+            const int o = w * tpw + sub, S = G * tpw;
+            auto upto = [&](int x) { return x <= o ? 0 : (x - o + S - 1) / S; };
+            int prev = 0;
+#pragma unroll
+            for (int g = 0; g < kLayerInputs; ++g) {
+                const int end = a.gend32[g];
+                n += (upto(end) - upto(prev)) * nq(a, g, kpart, P);
+                prev = end;
+            }
+        }
+        return n;
+    }
+};
+
+// Fills the schedule fields of `a` for a grid of G workgroups (the launcher
+// calls it; exposed for the host-side schedule tests).
+void plan_layer_schedule(LayerArgs &a, int G, bool b3);
 
 // Whether one launch can run the block: 1..4 tokens, every K at least one
 // 256-column block per wave, all token codes in LDS and all input chunks in
