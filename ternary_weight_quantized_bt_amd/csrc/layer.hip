@@ -24,8 +24,8 @@
 // group, then token, then column), are dealt to the waves in contiguous
 // spans of 64 x kLayerUnits chunks, lane l taking every 64th chunk from l
 // (each load one contiguous KiB per wave).  A span touches only a few
-// (group, token) rows (rows are >= 256 chunks long); their boundaries are
-// found with wave-uniform arithmetic, each lane keeps one running max per
+// (group, token) rows (rows are >= 256 chunks long); the host lists them
+// per wave in the kernel arguments, each lane keeps one running max per
 // row, DPP wave reductions (quant.hpp) fold them and one lane per row folds
 // the result into LDS with an atomic max.  After a barrier every chunk is
 // rounded from the registers and its codes stored in LDS; code sums are
@@ -42,6 +42,7 @@
 // per tile), and the epilogue dequantizes.
 
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "base3.hpp"
@@ -53,7 +54,6 @@ namespace bt {
 
 namespace {
 
-constexpr int kLayerWaves = 16;
 constexpr int kLayerThreads = kLayerWaves * kWave;
 constexpr int kLayerSplit = 8;  // K split over 8 waves: two tiles per iteration
 // Slot loads in flight per wave: 3 measured fastest on the 70B-class stream
@@ -68,12 +68,10 @@ constexpr int kLayerSplitB3 = 4;
 constexpr int64_t kLayerLdsMaxB3 = 80 * 1024;
 // An iteration's fixed cost in base-3 tile columns (8 KiB of streaming).
 constexpr int kIterCostB3 = 2;
-constexpr int kLayerUnits = 8;  // input chunks held per lane
 constexpr int64_t kLayerLdsMax = 128 * 1024;  // token codes of all four inputs
 constexpr int64_t kLayerMinK = (int64_t)kTileCols * kLayerSplit;  // a block per wave
-// (group, token) rows one wave's 64 * kLayerUnits consecutive chunks can
-// touch: rows are at least kLayerMinK / 8 = 256 chunks long.
-constexpr int kWaveRows = kWave * kLayerUnits / (kLayerMinK / 8) + 2;
+static_assert(kWaveRows == kLayerSpan / (kLayerMinK / 8) + 2,
+              "rows a span can touch: rows are at least kLayerMinK / 8 chunks long");
 
 // Projection -> input group.
 __host__ __device__ constexpr int proj_group(int p) { return p < 3 ? 0 : (p == 3 ? 1 : (p < 6 ? 2 : 3)); }
@@ -124,84 +122,71 @@ void layer_dot4_kernel(LayerArgs a) {
     static_assert(kLayerProj <= WAVES, "one wave per weight scale");
     constexpr int TPW = WAVES / P;
     constexpr int kKeys = kLayerInputs * NT;
-    constexpr int kSpan = kWave * kLayerUnits;  // chunks per wave
     extern __shared__ __attribute__((aligned(16))) int8_t codes[];
     __shared__ int red[2][WAVES][NT][16];
     __shared__ uint32_t s_amax[kKeys];  // max |x| bits per (group, token)
     __shared__ uint32_t s_sum[kKeys];   // code sum per (group, token)
     __shared__ float s_ws[kLayerProj];  // weight scales
 
-    // The argument block (some 560 bytes) is read throughout the setup below
-    // in chains of dependent scalar loads, and it starts every launch outside
-    // the scalar cache: touch each of its 64-byte lines first, all loads in
-    // flight together, so the chains then hit the cache instead of paying a
-    // miss per line in turn.
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // The argument block is read throughout the setup below in chains of
+    // dependent scalar loads, and it starts every launch outside the scalar
+    // cache: touch each 64-byte line of its head and this wave's row table
+    // first, all loads in flight together, so the chains then hit the cache
+    // instead of paying a miss per line in turn.
+    // The wave's row table is read in the same batch, as 16 words (its
+    // 16-bit fields sit at offsets a scalar load cannot take on their own).
+    uint32_t wt[16];
     {
         const auto *ka = (const __attribute__((address_space(4))) uint32_t *)
             __builtin_amdgcn_kernarg_segment_ptr();
-        constexpr int kWords = (int)(sizeof(LayerArgs) / 4);
+        constexpr int kWords = (int)(offsetof(LayerArgs, wrows) / 4);
         static_assert(kWords <= 160, "ten 64-byte lines");
+        static_assert(offsetof(LayerArgs, wrows) % 4 == 0, "word-aligned row tables");
         uint32_t t[10];
 #pragma unroll
         for (int i = 0; i < 10; ++i) t[i] = ka[min(16 * i, kWords - 1)];
+        const auto *kw = ka + kWords + 16 * wave;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wt[i] = kw[i];
         asm volatile("" : : "s"(t[0]), "s"(t[1]), "s"(t[2]), "s"(t[3]), "s"(t[4]),
                      "s"(t[5]), "s"(t[6]), "s"(t[7]), "s"(t[8]), "s"(t[9]));
+        asm volatile("" : : "s"(wt[0]), "s"(wt[1]), "s"(wt[2]), "s"(wt[3]), "s"(wt[4]),
+                     "s"(wt[5]), "s"(wt[6]), "s"(wt[7]), "s"(wt[8]), "s"(wt[9]),
+                     "s"(wt[10]), "s"(wt[11]), "s"(wt[12]), "s"(wt[13]), "s"(wt[14]),
+                     "s"(wt[15]));
     }
-    const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int h = lane / 16;
     const int nvalid = (int)min((int64_t)NT, a.N);
     const int kpart = wave % P, sub = wave / P;
     // ---- prologue, part 1: this wave's input chunks into registers ----
-    // Wave w owns chunks [w * kSpan, (w + 1) * kSpan) of the sequence; lane l
-    // holds chunks w * kSpan + 64c + l (c < kLayerUnits), so every load is one
-    // contiguous KiB per wave.  The (at most kWaveRows) rows the span touches
-    // are found with wave-uniform arithmetic: row r starts at span offset
-    // st[r] and a chunk at offset d lies in row #{r >= 1 : d >= st[r]}.
-    const int64_t units = a.uoff[kLayerInputs];
-    const int64_t u0 = (int64_t)wave * kSpan;
-    const int nlive = (int)max((int64_t)0, min((int64_t)kSpan, units - u0));
+    // Lane l holds chunks w * kLayerSpan + 64c + l (c < kLayerUnits) of the
+    // sequence, so every load is one contiguous KiB per wave; the rows the
+    // span touches come from the wave's table (LayerWaveRows, made on the
+    // host).
+    static_assert(offsetof(LayerWaveRows, src) == 0 && offsetof(LayerWaveRows, dst) == 32 &&
+                      offsetof(LayerWaveRows, st) == 48 && offsetof(LayerWaveRows, key) == 56 &&
+                      offsetof(LayerWaveRows, nlive) == 60 && offsetof(LayerWaveRows, nrow) == 62,
+                  "row table words");
+    const int nlive = (int16_t)(wt[15] & 0xFFFFu);
+    const int nrow = (int16_t)(wt[15] >> 16);
     const T *rsrc[kWaveRows];  // element of span offset 0 in row r's layout
     int rdst[kWaveRows];       // LDS byte of span offset 0 in row r's layout
     int rkey[kWaveRows];       // group * NT + token of row r
     int st[kWaveRows];         // span offset where row r starts
-    int nrow = 0;              // rows with live chunks
-    {
-        const int64_t u = min(u0, units - 1);
-        int g = 0;
 #pragma unroll
-        for (int i = 1; i < kLayerInputs; ++i) g += u >= a.uoff[i] ? 1 : 0;
-        int64_t cpr = sel(a.K, g) / 8;
-        int64_t j = (u - sel(a.uoff, g)) / cpr;
-        int64_t start = sel(a.uoff, g) + j * cpr - u0;  // <= 0
-#pragma unroll
-        for (int r = 0; r < kWaveRows; ++r) {
-            const bool real = g < kLayerInputs;
-            const int gg = real ? g : kLayerInputs - 1;
-            const int64_t Kg = sel(a.K, gg);
-            st[r] = real ? (int)start : INT32_MAX;
-            rkey[r] = real ? g * NT + (int)j : 0;
-            // (integer arithmetic: the base may lie before the buffer; only
-            // base + 8d for offsets d inside the row is ever dereferenced)
-            rsrc[r] = reinterpret_cast<const T *>(
-                reinterpret_cast<uintptr_t>(sel(a.x, gg)) +
-                (uintptr_t)((j * Kg - 8 * start) * (int64_t)sizeof(T)));
-            rdst[r] = (int)(sel(a.xoff, gg) + j * Kg - 8 * start);
-            nrow += (real && start < nlive) ? 1 : 0;
-            start += cpr;
-            if (++j == a.N) {
-                j = 0;
-                ++g;
-                cpr = g < kLayerInputs ? sel(a.K, g) / 8 : 1;
-            }
-        }
+    for (int r = 0; r < kWaveRows; ++r) {
+        rsrc[r] = reinterpret_cast<const T *>(((uint64_t)wt[2 * r + 1] << 32) | wt[2 * r]);
+        rdst[r] = (int)wt[8 + r];
+        rkey[r] = (int)((wt[14] >> (8 * r)) & 0xFFu);
+        st[r] = (int16_t)((wt[12 + r / 2] >> (16 * (r % 2))) & 0xFFFFu);
     }
     // Dead lanes (past the sequence) re-read the last chunk of the last row;
     // a wave with no live chunk issues no load (the prologue's loads queue
     // behind one another, and at one 70B-class token three of the 16 waves
     // hold nothing).
-    const T *last = static_cast<const T *>(a.x[kLayerInputs - 1]) +
-                    a.N * a.K[kLayerInputs - 1] - 8;
+    const T *last = static_cast<const T *>(a.xlast);
     Chunk<T> raw[kLayerUnits];
     int rowof[kLayerUnits];
     if (nlive == 0) {
@@ -727,6 +712,48 @@ LayerArgs make_layer_args(const uint8_t *const w[kLayerProj], const int64_t M[kL
         const int64_t Kp = a.K[proj_group(p)];
         a.wscale[p] = reinterpret_cast<const float *>(
             w[p] + (b3 ? b3_code_bytes(M[p], Kp) : M[p] * Kp / 4));
+    }
+    // The inputs are bf16 (layer_fusable); the prologue's tables address them
+    // in 2-byte elements.
+    constexpr int64_t kElem = 2;
+    a.xlast = reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(x[kLayerInputs - 1]) +
+                                             (uintptr_t)((N * K[kLayerInputs - 1] - 8) * kElem));
+    // Each wave's span of the chunk sequence: the row holding its first chunk
+    // (the last chunk of the sequence for a span past the end), then the rows
+    // that follow it, kWaveRows in all (past the fourth input: no row).
+    const int64_t units = uo;
+    for (int wv = 0; wv < kLayerWaves; ++wv) {
+        LayerWaveRows &t = a.wrows[wv];
+        const int64_t u0 = (int64_t)wv * kLayerSpan;
+        const int64_t nlive = std::max<int64_t>(0, std::min<int64_t>(kLayerSpan, units - u0));
+        const int64_t u = std::min(u0, units - 1);
+        int g = 0;
+        while (g + 1 < kLayerInputs && u >= a.uoff[g + 1]) ++g;
+        int64_t cpr = K[g] / 8;
+        int64_t j = (u - a.uoff[g]) / cpr;
+        int64_t start = a.uoff[g] + j * cpr - u0;  // <= 0
+        int nrow = 0;
+        for (int r = 0; r < kWaveRows; ++r) {
+            const bool real = g < kLayerInputs;
+            const int gg = real ? g : kLayerInputs - 1;
+            // span offsets d only meet st[r] for r >= 1, where 0 < start; any
+            // value >= kLayerSpan compares like "no row"
+            t.st[r] = (int16_t)(real ? std::min<int64_t>(std::max<int64_t>(start, -kLayerSpan), kLayerSpan)
+                                     : kLayerSpan);
+            t.key[r] = (uint8_t)(real ? g * nt + j : 0);
+            t.src[r] = reinterpret_cast<const void *>(reinterpret_cast<uintptr_t>(x[gg]) +
+                                                      (uintptr_t)((j * K[gg] - 8 * start) * kElem));
+            t.dst[r] = (int)(a.xoff[gg] + j * K[gg] - 8 * start);
+            nrow += (real && start < nlive) ? 1 : 0;
+            start += cpr;
+            if (++j == N) {
+                j = 0;
+                ++g;
+                cpr = g < kLayerInputs ? K[g] / 8 : 1;
+            }
+        }
+        t.nlive = (int16_t)nlive;
+        t.nrow = (int16_t)nrow;
     }
     return a;
 }

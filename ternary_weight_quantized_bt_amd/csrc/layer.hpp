@@ -9,6 +9,30 @@ namespace bt {
 
 constexpr int kLayerProj = BT_LAYER_PROJ;     // q, k, v, o, gate, up, down
 constexpr int kLayerInputs = BT_LAYER_INPUTS;  // x0 -> q,k,v; x1 -> o; x2 -> gate,up; x3 -> down
+constexpr int kLayerWaves = 16;  // waves per workgroup
+constexpr int kLayerUnits = 8;   // input chunks (8 elements) held per lane in the prologue
+constexpr int kLayerSpan = kWave * kLayerUnits;  // chunks per wave
+// (group, token) rows one wave's span can touch: rows are at least 256
+// chunks long (K >= 2048), so a 512-chunk span meets at most four.
+constexpr int kWaveRows = 4;
+
+// One wave's share of the prologue's input sequence (the four inputs seen as
+// one run of 8-element chunks: input group, then token, then column), made on
+// the host; the same in every workgroup.  Wave w owns chunks
+// [w * kLayerSpan, (w + 1) * kLayerSpan); the chunk at span offset d lies in
+// row #{r >= 1 : d >= st[r]}.  64 bytes: one scalar load per wave.
+struct LayerWaveRows {
+    const void *src[kWaveRows];  // element of span offset 0 in row r's layout (integer
+                                 // arithmetic: may lie outside the input; only the
+                                 // offsets inside row r are read through it)
+    int dst[kWaveRows];          // LDS byte of span offset 0 in row r's layout
+    int16_t st[kWaveRows];       // span offset where row r starts, clamped to
+                                 // [-kLayerSpan, kLayerSpan] (kLayerSpan: no row)
+    uint8_t key[kWaveRows];      // group * NT + token of row r (0: no row)
+    int16_t nlive;               // chunks of the span inside the sequence
+    int16_t nrow;                // rows that start before offset nlive (row 0 always does)
+};
+static_assert(sizeof(LayerWaveRows) == 64, "one 64-byte scalar load per wave");
 
 struct LayerArgs {
     const uint8_t *packed[kLayerProj];
@@ -42,6 +66,8 @@ struct LayerArgs {
     // 1024-column tile columns, and the decode table sits at LDS byte tab32).
     int b3, tab32;
     const float *wscale[kLayerProj];  // each projection's weight scale (packed tail)
+    const void *xlast;  // last chunk of the last input (dead lanes re-read it)
+    LayerWaveRows wrows[kLayerWaves];
 };
 
 // One workgroup's work under a LayerArgs schedule, shared by the kernel and

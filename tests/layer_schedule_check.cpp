@@ -9,10 +9,14 @@
 //     once), every wave with at least one block;
 //   - the closed-form slot count of each wave equals the walk over its
 //     iterations (the kernel's cursors stop after that many slots, and every
-//     wave of a workgroup runs the same iterations, each ending in a barrier).
+//     wave of a workgroup runs the same iterations, each ending in a barrier);
+//   - the prologue's per-wave input row tables (1 to 4 tokens) place every
+//     input chunk at its own element, LDS byte and (group, token) key.
 // Prints the schedule chosen for the 70B-class block; exit status 0 if every
 // check passes.
 #include <cstdio>
+#include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 #include <random>
 #include <vector>
@@ -85,6 +89,49 @@ void check(const int64_t M[7], const int64_t K[4], int G, bool b3) {
     for (int t = 0; t < total; ++t) CHECK(seen[t] == 1, "tile %d taken %d times", t, seen[t]);
 }
 
+// The prologue's per-wave row tables (bt::LayerWaveRows) for N tokens: every
+// live chunk of every wave's span, located the way the kernel locates it
+// (row #{r >= 1 : d >= st[r]}), addresses its own input element and LDS byte
+// and carries its (group, token) key; a table with one row holds all of its
+// span; dead spans hold nothing.
+void check_rows(const int64_t M[7], const int64_t K[4], int64_t N) {
+    if (!bt::layer_fusable(K, M, N, BT_BF16)) return;
+    const uint8_t *w[7] = {};
+    const void *x[4];
+    void *y[7] = {};
+    for (int g = 0; g < 4; ++g) x[g] = reinterpret_cast<const void *>((uintptr_t)(g + 1) << 36);
+    const bt::LayerArgs a = bt::make_layer_args(w, M, K, x, y, N, BT_BF16, false);
+    const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
+    int64_t units = 0;
+    for (int g = 0; g < 4; ++g) units += N * K[g] / 8;
+    for (int wv = 0; wv < bt::kLayerWaves; ++wv) {
+        const bt::LayerWaveRows &t = a.wrows[wv];
+        const int64_t u0 = (int64_t)wv * bt::kLayerSpan;
+        const int64_t live = std::max<int64_t>(0, std::min<int64_t>(bt::kLayerSpan, units - u0));
+        CHECK(t.nlive == live, "N %lld wave %d: nlive %d, want %lld", (long long)N, wv, t.nlive,
+              (long long)live);
+        CHECK(t.nrow >= 1 && t.nrow <= bt::kWaveRows, "wave %d: nrow %d", wv, t.nrow);
+        for (int d = 0; d < live; ++d) {
+            int r = 0;
+            for (int k = 1; k < bt::kWaveRows; ++k) r += d >= t.st[k] ? 1 : 0;
+            // the chunk's place by direct search
+            int64_t u = u0 + d, g = 0;
+            while (u >= N * K[g] / 8) u -= N * K[g] / 8, ++g;
+            const int64_t j = u / (K[g] / 8), c = u % (K[g] / 8);
+            const uintptr_t want_src = (uintptr_t)x[g] + (uintptr_t)(2 * (j * K[g] + 8 * c));
+            const uintptr_t got_src = (uintptr_t)t.src[r] + (uintptr_t)(2 * 8 * d);
+            CHECK(r < t.nrow, "N %lld wave %d chunk %d: row %d of %d", (long long)N, wv, d, r, t.nrow);
+            CHECK(got_src == want_src, "N %lld wave %d chunk %d: source", (long long)N, wv, d);
+            CHECK((int64_t)t.dst[r] + 8 * d == a.xoff[g] + j * K[g] + 8 * c,
+                  "N %lld wave %d chunk %d: LDS byte", (long long)N, wv, d);
+            CHECK(t.key[r] == g * nt + j, "N %lld wave %d chunk %d: key %d, want %lld",
+                  (long long)N, wv, d, t.key[r], (long long)(g * nt + j));
+        }
+    }
+    // the dead lanes' chunk: the last one of the last input
+    CHECK((uintptr_t)a.xlast == (uintptr_t)x[3] + (uintptr_t)(2 * (N * K[3] - 8)), "xlast");
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -94,6 +141,13 @@ int main(int argc, char **argv) {
         const int64_t K[4] = {8192, 8192, 8192, 28672};
         check(M, K, 256, false);
         check(M, K, 256, true);
+        for (int n = 1; n <= 4; ++n) check_rows(M, K, n);
+        const int64_t M2[7] = {2560, 640, 640, 2560, 6912, 6912, 2560};
+        const int64_t K2[4] = {2560, 2560, 2560, 6912};
+        for (int n = 1; n <= 4; ++n) check_rows(M2, K2, n);
+        const int64_t M3[7] = {2048, 2048, 2048, 2048, 2048, 2048, 2048};
+        const int64_t K3[4] = {2048, 2048, 2048, 2048};
+        for (int n = 1; n <= 4; ++n) check_rows(M3, K3, n);
         const uint8_t *w[7] = {};
         const void *x[4] = {};
         void *y[7] = {};
@@ -117,6 +171,7 @@ int main(int argc, char **argv) {
         }
         for (int p = 0; p < 7; ++p) M[p] = 16 * (int64_t)pick(1, 600);
         check(M, K, pick(1, 300), b3);
+        if (!b3) check_rows(M, K, pick(1, 4));
     }
     std::printf("%s after %d random blocks (schedules: %d striding, %d two-class)\n",
                 g_fail ? "FAILED" : "ok", cases, g_modes[0], g_modes[1]);
