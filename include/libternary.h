@@ -261,7 +261,8 @@ bt_status bt_quant_act(const void *x, bt_dtype x_dtype, int64_t N, int64_t K,
  *
  * bt_ternary_gemv is the decode path (few tokens: weights are streamed once
  * from HBM with 128-bit loads, unpacked in registers, and dotted with the
- * int8 activations, with int8 matrix cores once N is large enough to pay);
+ * int8 activations -- on the int8 matrix cores from 5 tokens, and from 2
+ * tokens where the matrix is tall (M >= 4096) or its rows long);
  * bt_ternary_gemm is the prefill path (many tokens: tiled int8 matrix-core
  * product).  Both accept any N >= 0 and return identical results.
  * ---------------------------------------------------------------------- */
@@ -313,17 +314,21 @@ bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
  * identical to calling bt_quant_act followed by bt_ternary_gemv /
  * bt_ternary_gemm per projection, whatever the launch structure:
  *   - 1..4 tokens, every K >= 2048, the codes of all four inputs within
- *     128 KiB and 8-element input chunks within 8 per thread of a 1024-thread
- *     workgroup (e.g. 1 token of an 8192/28672 block, up to 4 of a
- *     2560/6912 block): ONE launch for the whole block.  The kernel
+ *     128 KiB, 8-element input chunks within 8 per thread of a 1024-thread
+ *     workgroup, and from 2 tokens on at most 64 / 20 / 12 MB of packed
+ *     weights at 2 / 3 / 4 tokens (beyond that the matrix-core launch below
+ *     is faster) -- e.g. 1 token of an 8192/28672 block, up to 3 of a
+ *     2560/6912 block: ONE launch for the whole block.  The kernel
  *     quantizes all four inputs in its prologue and streams the seven
  *     weight matrices back to back ([PREP] "Stage 1" lists them), so the
  *     four inputs must all be valid when the call is made -- which is what
  *     this interface takes.  The workspace is not touched.
- *   - otherwise: one launch that quantizes the four inputs into the
- *     workspace (for a few tokens with short rows the per-group decode
- *     kernel quantizes its own input instead), then one product launch per
- *     group.
+ *   - otherwise, from 2 tokens on: one launch that quantizes the four
+ *     inputs into the workspace, then one matrix-core launch for all four
+ *     groups (decode below BT_PREFILL_MIN_N tokens, prefill from there).
+ *   - otherwise (1 token of a block too large for one launch): one decode
+ *     launch per group, each quantizing its own input in its prologue where
+ *     the row fits (the other inputs are quantized by one launch first).
  *   - with BT_LAYER_PER_GROUP in io->flags: the groups one after the other,
  *     each quantizing its own input (in the decode kernel, or by a launch of
  *     its own) before its product -- the order of a decoder whose inputs

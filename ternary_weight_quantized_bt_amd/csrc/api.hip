@@ -469,6 +469,20 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
     }
     const LayerWs ws = carve(Kin, N, workspace);
     const bool per_group = (io->flags & BT_LAYER_PER_GROUP) != 0;
+    // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
+    static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
+    static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
+    int64_t rows[BT_LAYER_INPUTS];
+    for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
+        rows[i] = 0;
+        for (int j = 0; j < kCount[i]; ++j) rows[i] += L->M[kFirst[i] + j];
+    }
+    // From 2 tokens on, a block that is not one launch runs its four groups
+    // on the matrix cores in one launch (faster than per-group dot4 launches
+    // on every block too large for the one-launch kernel: 70B-class at 2
+    // tokens 3.37 vs 5.51 ms per 80 blocks, 7B-class at 3 tokens 0.52 vs 1.08
+    // ms per 24).  At 1 token each group runs on its own dot4 launch.
+    const bool four_groups = N >= 2;
     // The four inputs are all valid at the call: unless asked for per-group
     // launches, the ones that need codes in the workspace are quantized in
     // one launch up front.
@@ -477,7 +491,7 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
         bt::QuantJobs jobs{};
         int count = 0;
         for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
-            if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, Kin[i], io->x_dtype)) continue;
+            if (!four_groups && bt::decode_fuses_quant(N, rows[i], Kin[i], io->x_dtype)) continue;
             jobs.x[count] = io->x[i];
             jobs.K[count] = Kin[i];
             jobs.xq[count] = ws.xq[i];
@@ -489,9 +503,6 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
         if (e != hipSuccess) return hip_status(e, fn);
         quantized = true;
     }
-    // groups: {q,k,v} <- x0, {o} <- x1, {gate,up} <- x2, {down} <- x3
-    static const int kFirst[BT_LAYER_INPUTS] = {0, 3, 4, 6};
-    static const int kCount[BT_LAYER_INPUTS] = {3, 1, 2, 1};
     bt::Group groups[BT_LAYER_INPUTS];
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
         bt::Group &g = groups[i];
@@ -508,7 +519,7 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
         g.N = N;
         g.ydt = io->y_dtype;
     }
-    if (quantized && N > bt::kDot4MaxN) {
+    if (quantized && four_groups) {
         // matrix-core decode or prefill: the four groups in one launch
         const hipError_t e = N < BT_PREFILL_MIN_N
                                  ? bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s)
@@ -518,7 +529,7 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
         const bt::Group &g = groups[i];
         hipError_t e;
-        if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, Kin[i], io->x_dtype)) {
+        if (N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, rows[i], Kin[i], io->x_dtype)) {
             // one launch: the decode kernel quantizes its input itself
             e = bt::launch_decode_fused(g, io->x[i], io->x_dtype, s);
         } else {

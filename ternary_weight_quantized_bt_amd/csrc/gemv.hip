@@ -398,17 +398,36 @@ int device_cus() {
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s);
 
+// From 2 tokens on, the dot4 kernel reads every token's activation words from
+// LDS for each weight slot (four 16-byte reads per token per slot), so it
+// turns LDS- and ALU-bound where the weight stream is long, while the
+// matrix-core kernel costs about the same for any N <= 16 but needs many row
+// tiles to fill the chip.  Measured per call (bf16 out, each call on its own
+// weight copy): at 2 tokens dot4 is as fast or faster except on the longest
+// rows (8192 x 28672: 17.6 vs 16.4 us); at 3-4 tokens it is faster on short
+// groups (2560 x 2560 and 2560 x 6912: 5.1-6.7 vs 5.8-7.8 us) and slower on
+// tall ones (6912 x 2560 at 3 tokens: 6.5 vs 6.0 us; 8192 x 8192 at 4: 9.6 vs
+// 8.2 us); rows whose codes exceed its LDS (NT * K above 64 KiB) make it read
+// them from global memory at twice the time (8192 x 28672 at 3 tokens: 35.3
+// vs 16.8 us).
+bool decode_dot4(int64_t N, int64_t M, int64_t K) {
+    if (N < 1 || N > kDot4MaxN) return false;
+    if (N == 1) return true;
+    if (tokens_per_pass(N) * K > kDecLdsMax) return false;
+    return M < 4096 || (N == 2 && K < 16384);
+}
+
 hipError_t launch_decode(const Group &g, hipStream_t s) {
     if (g.N == 0) return hipSuccess;
     const GroupArgs a = make_group_args(g);
-    if (g.N > kDot4MaxN) return launch_mfma_decode(a, s);
+    if (!decode_dot4(g.N, group_rows(g), g.K)) return launch_mfma_decode(a, s);
     const DecodeX dx{nullptr, g.xq, g.xs, g.xsum};
     const int mode = tokens_per_pass(g.N) * g.K <= kDecLdsMax ? 1 : 2;
     return launch_dec_any(a, dx, mode, BT_BF16, s);
 }
 
-bool decode_fuses_quant(int64_t N, int64_t K, bt_dtype xdt) {
-    return N >= 1 && N <= kDot4MaxN && fused_fits(N, K, xdt);
+bool decode_fuses_quant(int64_t N, int64_t M, int64_t K, bt_dtype xdt) {
+    return decode_dot4(N, M, K) && fused_fits(N, K, xdt);
 }
 
 hipError_t launch_decode_fused(const Group &g, const void *x, bt_dtype xdt, hipStream_t s) {

@@ -64,13 +64,22 @@ struct Group {
 };
 
 // Decode path (few tokens): 128-bit weight streaming + dot4, or skinny
-// matrix-core tiles once N is large enough.
+// matrix-core tiles where those are faster (decode_dot4).
 hipError_t launch_decode(const Group &g, hipStream_t s);
+// Whether the decode of N tokens over a group of M rows (all its
+// projections) and K columns runs on the dot4 kernel (else the matrix cores).
+bool decode_dot4(int64_t N, int64_t M, int64_t K);
+// Rows of a group (all its projections).
+inline int64_t group_rows(const Group &g) {
+    int64_t m = 0;
+    for (int j = 0; j < g.count; ++j) m += g.p[j].M;
+    return m;
+}
 // Decode path with the activation quantization fused into the kernel's
 // prologue (x is the float / bf16 input of the group).  Only for shapes where
-// decode_fuses_quant(N, K) holds.
-bool decode_fuses_quant(int64_t N, int64_t K, bt_dtype xdt);
-// Matrix-core decode (kDot4MaxN < N < BT_PREFILL_MIN_N) of up to four groups,
+// decode_fuses_quant(N, M, K) holds.
+bool decode_fuses_quant(int64_t N, int64_t M, int64_t K, bt_dtype xdt);
+// Matrix-core decode (1 < N < BT_PREFILL_MIN_N) of up to four groups,
 // each with its own quantized input, in one launch; results equal
 // launch_decode per group.
 hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s);
@@ -84,7 +93,7 @@ hipError_t launch_prefill_groups(const Group *groups, int count, hipStream_t s);
 // Compute units of the current device (cached per device).
 int device_cus();
 
-// Largest N for which launch_decode uses the dot4 kernel.
+// Largest N for which launch_decode may use the dot4 kernel.
 constexpr int64_t kDot4MaxN = 4;
 
 // The per-layer driver behind bt_layer_forward with its scratch passed

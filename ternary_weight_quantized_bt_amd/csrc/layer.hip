@@ -650,6 +650,20 @@ void plan_layer_schedule(LayerArgs &a, int G, bool b3) {
         plan_schedule<kLayerWaves / kLayerSplit>(a, G, kIterCostBlocks);
 }
 
+// Largest 2-bit block (packed bytes) that the one-launch kernel takes at N
+// tokens.  From 2 tokens on its dot4 products read every token's activation
+// words from LDS for each weight slot (four 16-byte reads per token), so its
+// time grows with N times the weight bytes, while the four-group matrix-core
+// decode (plus one quantization launch) costs a fixed ~14 us plus the
+// stream.  Measured per block (us, one-launch vs matrix cores): 2 tokens:
+// 11.3 MB 12.0 vs 15.3, 50.6 MB 19.8 vs 21.3, 79.3 MB 25.3 vs 24.4; 3 tokens:
+// 11.3 MB 13.2 vs 15.6, 17.4 MB 16.2 vs 16.9; 4 tokens: 11.3 MB 15.2 vs 15.7,
+// 17.4 MB 18.9 vs 16.7.
+static int64_t fused_max_bytes(int64_t N) {
+    constexpr int64_t kMB = 1000000;
+    return N <= 1 ? INT64_MAX : N == 2 ? 64 * kMB : N == 3 ? 20 * kMB : 12 * kMB;
+}
+
 bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], int64_t N,
                    bt_dtype xdt, bool b3) {
     if (N < 1 || N > 4) return false;
@@ -660,9 +674,14 @@ bool layer_fusable(const int64_t K[kLayerInputs], const int64_t M[kLayerProj], i
         if (b3 && (K[g] % kB3Cols != 0 || K[g] < (int64_t)kB3Cols * kLayerSplitB3)) return false;
         sumk += K[g];
     }
-    int64_t tiles = 0;
-    for (int p = 0; p < kLayerProj; ++p) tiles += M[p] / kTileRows;
+    int64_t tiles = 0, bytes = 0;
+    for (int p = 0; p < kLayerProj; ++p) {
+        tiles += M[p] / kTileRows;
+        bytes += M[p] * K[proj_group(p)] / 4;
+    }
     if (tiles >= (int64_t)1 << 30) return false;  // tile bookkeeping is 32-bit
+    // (base-3 blocks have no matrix-core path: the one launch is their fastest)
+    if (!b3 && bytes > fused_max_bytes(N)) return false;
     const int nt = N == 1 ? 1 : (N == 2 ? 2 : 4);
     if (nt * sumk > (b3 ? kLayerLdsMaxB3 : kLayerLdsMax)) return false;
     const int64_t units = N * sumk / 8;

@@ -271,8 +271,19 @@ def test_layer_one_launch_choice():
     assert bt.bt_layer_one_launch(_layer(big), 1, bt.BT_BF16) == 1
     assert bt.bt_layer_one_launch(_layer(big), 2, bt.BT_BF16) == 0   # chunks exceed registers
     assert bt.bt_layer_one_launch(_layer(big), 1, bt.BT_F32) == 0
-    assert bt.bt_layer_one_launch(_layer(small), 4, bt.BT_BF16) == 1
+    assert bt.bt_layer_one_launch(_layer(small), 3, bt.BT_BF16) == 1
+    # 17.4 MB of packed weights: above the 12 MB up to which one launch beats
+    # the matrix-core decode at 4 tokens
+    assert bt.bt_layer_one_launch(_layer(small), 4, bt.BT_BF16) == 0
     assert bt.bt_layer_one_launch(_layer(small), 5, bt.BT_BF16) == 0
+    # a 1B-class block (11.3 MB) still runs as one launch at 4 tokens; a
+    # 13B-class one (79.3 MB) only at 1 token (64 MB limit at 2)
+    tiny = [(2048, 2048), (512, 2048), (512, 2048), (2048, 2048), (5632, 2048),
+            (5632, 2048), (2048, 5632)]
+    assert bt.bt_layer_one_launch(_layer(tiny), 4, bt.BT_BF16) == 1
+    b13 = [(5120, 5120)] * 4 + [(13824, 5120), (13824, 5120), (5120, 13824)]
+    assert bt.bt_layer_one_launch(_layer(b13), 1, bt.BT_BF16) == 1
+    assert bt.bt_layer_one_launch(_layer(b13), 2, bt.BT_BF16) == 0
     assert bt.bt_layer_one_launch(_layer(LAYER), 1, bt.BT_BF16) == 0  # K below 2048
     bad = list(LAYER)
     bad[1] = (32, 512)

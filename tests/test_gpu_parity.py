@@ -175,6 +175,28 @@ def test_batched_decode_staging_modes(M, K, N):
             assert_rel_close(as_f64(y), ref["y"], RTOL[ydt], f"M={M} K={K} N={N} ydt={ydt}")
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (4096, 2304, 2),    # tall group, 2 tokens: dot4
+    (4096, 2304, 3),    # tall group, 3 tokens: matrix cores
+    (4112, 2304, 4),    # tall, odd tile count, 4 tokens: matrix cores
+    (4096, 16640, 2),   # tall with long rows, 2 tokens: matrix cores
+    (48, 16640, 2),     # short group with long rows, 2 tokens: dot4
+    (64, 17408, 3),     # codes of 4 token slots beyond the dot4 kernel's LDS: matrix cores
+])
+def test_decode_kernel_choice_few_tokens(M, K, N):
+    """2..4 tokens run on the dot4 kernel or on the matrix cores depending on
+    the group's shape; either way exact in int32 against the oracle, and
+    equal bit for bit to the prefill kernel."""
+    ref_packed, ref, packed, xq, xs, xsum = _case(M, K, N, 3 * M + K + N)
+    for ydt in (bt.BT_I32, bt.BT_BF16):
+        y = bt.gemv(packed, M, K, xq, xs, xsum, ydt)
+        assert torch.equal(y, bt.gemm(packed, M, K, xq, xs, xsum, ydt)), (M, K, N, ydt)
+        if ydt == bt.BT_I32:
+            assert_equal(to_np(y), ref["acc"], f"M={M} K={K} N={N}")
+        else:
+            assert_rel_close(as_f64(y), ref["y"], RTOL[ydt], f"M={M} K={K} N={N}")
+
+
 def test_batched_decode_three_k_phases_sampled():
     """Rows too long for LDS (12 tokens x 25600 columns): three K phases with
     int32 partial sums carried in LDS, several tiles per workgroup, a ragged
