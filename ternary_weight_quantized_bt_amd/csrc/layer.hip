@@ -137,7 +137,9 @@ void layer_dot4_kernel(LayerArgs a) {
     // instead of paying a miss per line in turn.
     // The wave's row table is read in the same batch, as 16 words (its
     // 16-bit fields sit at offsets a scalar load cannot take on their own).
+    // So is the word listing the inputs this workgroup reads.
     uint32_t wt[16];
+    uint32_t needw;
     {
         const auto *ka = (const __attribute__((address_space(4))) uint32_t *)
             __builtin_amdgcn_kernarg_segment_ptr();
@@ -150,8 +152,9 @@ void layer_dot4_kernel(LayerArgs a) {
         const auto *kw = ka + kWords + 16 * wave;
 #pragma unroll
         for (int i = 0; i < 16; ++i) wt[i] = kw[i];
+        needw = ka[offsetof(LayerArgs, need) / 4 + min((int)blockIdx.x, kLayerNeedWgs - 1) / 8];
         asm volatile("" : : "s"(t[0]), "s"(t[1]), "s"(t[2]), "s"(t[3]), "s"(t[4]),
-                     "s"(t[5]), "s"(t[6]), "s"(t[7]), "s"(t[8]), "s"(t[9]));
+                     "s"(t[5]), "s"(t[6]), "s"(t[7]), "s"(t[8]), "s"(t[9]), "s"(needw));
         asm volatile("" : : "s"(wt[0]), "s"(wt[1]), "s"(wt[2]), "s"(wt[3]), "s"(wt[4]),
                      "s"(wt[5]), "s"(wt[6]), "s"(wt[7]), "s"(wt[8]), "s"(wt[9]),
                      "s"(wt[10]), "s"(wt[11]), "s"(wt[12]), "s"(wt[13]), "s"(wt[14]),
@@ -169,7 +172,6 @@ void layer_dot4_kernel(LayerArgs a) {
                       offsetof(LayerWaveRows, st) == 48 && offsetof(LayerWaveRows, key) == 56 &&
                       offsetof(LayerWaveRows, nlive) == 60 && offsetof(LayerWaveRows, nrow) == 62,
                   "row table words");
-    const int nlive = (int16_t)(wt[15] & 0xFFFFu);
     const int nrow = (int16_t)(wt[15] >> 16);
     const T *rsrc[kWaveRows];  // element of span offset 0 in row r's layout
     int rdst[kWaveRows];       // LDS byte of span offset 0 in row r's layout
@@ -182,6 +184,13 @@ void layer_dot4_kernel(LayerArgs a) {
         rkey[r] = (int)((wt[14] >> (8 * r)) & 0xFFu);
         st[r] = (int16_t)((wt[12 + r / 2] >> (16 * (r % 2))) & 0xFFFFu);
     }
+    // A span lying only in inputs that none of this workgroup's tiles read
+    // is skipped: no loads, no codes (its LDS is never read).
+    const uint32_t need = blockIdx.x < kLayerNeedWgs ? (needw >> (4 * (blockIdx.x % 8))) & 0xFu : 0xFu;
+    bool wanted = false;
+#pragma unroll
+    for (int r = 0; r < kWaveRows; ++r) wanted |= r < nrow && ((need >> (rkey[r] / NT)) & 1u) != 0;
+    const int nlive = wanted ? (int16_t)(wt[15] & 0xFFFFu) : 0;
     // Dead lanes (past the sequence) re-read the last chunk of the last row;
     // a wave with no live chunk issues no load (the prologue's loads queue
     // behind one another, and at one 70B-class token three of the 16 waves
@@ -648,6 +657,40 @@ void plan_layer_schedule(LayerArgs &a, int G, bool b3) {
         plan_schedule<kLayerWaves / kLayerSplitB3>(a, G, kIterCostB3);
     else
         plan_schedule<kLayerWaves / kLayerSplit>(a, G, kIterCostBlocks);
+    // The input groups each workgroup's tiles read.  Under the two-class
+    // schedule a workgroup's tiles are two contiguous ranges, each spanning
+    // the groups from its first tile's to its last tile's; a striding
+    // workgroup with few iterations is walked, one with many reads all four.
+    const int tpw = kLayerWaves / (b3 ? kLayerSplitB3 : kLayerSplit);
+    const int total = a.tend32[kLayerProj - 1];
+    auto group_of_tile = [&](int t) {
+        int g = 0;
+        while (g + 1 < kLayerInputs && t >= a.gend32[g]) ++g;
+        return g;
+    };
+    auto range = [&](int g0, int n) -> uint32_t {  // tile groups [g0, g0 + n)
+        const int t0 = g0 * tpw, t1 = std::min((g0 + n) * tpw, total);
+        if (n <= 0 || t0 >= t1) return 0u;
+        const int lo = group_of_tile(t0), hi = group_of_tile(t1 - 1);
+        return ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+    };
+    for (auto &x : a.need) x = 0u;
+    for (int w = 0; w < std::min(G, kLayerNeedWgs); ++w) {
+        const LayerSched ls(a, w, G, tpw);
+        uint32_t m = 0u;
+        if (ls.sched) {
+            m = range(ls.sfirst, ls.nS) | range(ls.bfirst, ls.nB);
+        } else if ((int64_t)ls.nit * tpw <= 64) {
+            for (int it = 0; it < ls.nit; ++it)
+                for (int sg = 0; sg < tpw; ++sg) {
+                    const int t = ls.tile_for(it, sg);
+                    if (t < total) m |= 1u << group_of_tile(t);
+                }
+        } else {
+            m = 0xFu;
+        }
+        a.need[w / 8] |= m << (4 * (w % 8));
+    }
 }
 
 // Largest 2-bit block (packed bytes) that the one-launch kernel takes at N

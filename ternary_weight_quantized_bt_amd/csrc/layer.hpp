@@ -34,6 +34,10 @@ struct LayerWaveRows {
 };
 static_assert(sizeof(LayerWaveRows) == 64, "one 64-byte scalar load per wave");
 
+// Workgroups whose input needs are listed (LayerArgs::need); later ones read
+// all four inputs.
+constexpr int kLayerNeedWgs = 256;
+
 struct LayerArgs {
     const uint8_t *packed[kLayerProj];
     void *y[kLayerProj];
@@ -68,6 +72,10 @@ struct LayerArgs {
     const float *wscale[kLayerProj];  // each projection's weight scale (packed tail)
     const void *xlast;  // last chunk of the last input (dead lanes re-read it)
     LayerWaveRows wrows[kLayerWaves];
+    // Input groups that workgroup w's tiles read: bits 4 (w % 8) .. 4 (w % 8)
+    // + 3 of need[w / 8] (made with the schedule); the prologue skips the
+    // spans of the others.
+    uint32_t need[kLayerNeedWgs / 8];
 };
 
 // One workgroup's work under a LayerArgs schedule, shared by the kernel and
@@ -146,8 +154,9 @@ struct LayerSched {
     }
 };
 
-// Fills the schedule fields of `a` for a grid of G workgroups (the launcher
-// calls it; exposed for the host-side schedule tests).
+// Fills the schedule fields of `a`, and the input groups each workgroup
+// reads, for a grid of G workgroups (the launcher calls it; exposed for the
+// host-side schedule tests).
 void plan_layer_schedule(LayerArgs &a, int G, bool b3);
 
 // Whether one launch can run the block: 1..4 tokens, every K at least one

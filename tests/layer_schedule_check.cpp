@@ -11,7 +11,8 @@
 //     iterations (the kernel's cursors stop after that many slots, and every
 //     wave of a workgroup runs the same iterations, each ending in a barrier);
 //   - the prologue's per-wave input row tables (1 to 4 tokens) place every
-//     input chunk at its own element, LDS byte and (group, token) key.
+//     input chunk at its own element, LDS byte and (group, token) key, and
+//     the inputs a workgroup quantizes cover every tile it takes.
 // Prints the schedule chosen for the 70B-class block; exit status 0 if every
 // check passes.
 #include <cstdio>
@@ -60,6 +61,21 @@ void check(const int64_t M[7], const int64_t K[4], int G, bool b3) {
     std::vector<int> seen(total, 0);
     for (int wg = 0; wg < G; ++wg) {
         const bt::LayerSched ls(a, wg, G, tpw);
+        // the inputs the workgroup's prologue quantizes cover every tile it
+        // takes (exactly, under the two-class schedule)
+        {
+            uint32_t walk = 0;
+            for (int it = 0; it < ls.nit; ++it)
+                for (int s = 0; s < tpw; ++s) {
+                    const int t = ls.tile_for(it, s);
+                    if (t >= 0 && t < total) walk |= 1u << group_of_tile(a, t);
+                }
+            const uint32_t need =
+                wg < bt::kLayerNeedWgs ? (a.need[wg / 8] >> (4 * (wg % 8))) & 0xFu : 0xFu;
+            CHECK((walk & ~need) == 0, "wg %d reads inputs 0x%x, marked 0x%x", wg, walk, need);
+            CHECK(!a.sched || wg >= bt::kLayerNeedWgs || walk == need,
+                  "wg %d: two-class need 0x%x, walk 0x%x", wg, need, walk);
+        }
         for (int wave = 0; wave < kWaves; ++wave) {
             const int kpart = wave % P, sub = wave / P;
             int walk = 0;
@@ -155,6 +171,12 @@ int main(int argc, char **argv) {
         bt::plan_layer_schedule(a, 256, false);
         std::printf("70B-class block, 256 workgroups: sched %d, n0 %d, heavy %d/%d, light groups %d/%d\n",
                     a.sched, a.n0, a.heavy[0], a.heavy[1], a.scount[0], a.scount[1]);
+        int hist[16] = {};
+        for (int wg = 0; wg < 256; ++wg) ++hist[(a.need[wg / 8] >> (4 * (wg % 8))) & 0xFu];
+        std::printf("inputs read per workgroup (mask: workgroups):");
+        for (int m = 0; m < 16; ++m)
+            if (hist[m]) std::printf(" 0x%x: %d", m, hist[m]);
+        std::printf("\n");
     }
     std::mt19937 rng(20241021);
     auto pick = [&](int lo, int hi) { return std::uniform_int_distribution<int>(lo, hi)(rng); };
