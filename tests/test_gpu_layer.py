@@ -84,6 +84,31 @@ def test_small_layer_f32_inputs():
     run_layer(wl, 0, 5, bt.BT_F32)
 
 
+# Row counts give ragged 256-row tiles in every group; three K values.
+STREAM = W.Workload(
+    name="prefill_groups", index=12, description="four groups of different K in one launch",
+    shapes=((272, 2304), (48, 2304), (48, 2304), (2304, 1024), (1040, 2304), (1040, 2304),
+            (2304, 3328)),
+    layers=1, batches=(128, 257, 1000), x_dtype="bf16", y_dtype="bf16",
+    weight_dist="p0_0.4", act_dist="student_t4")
+
+
+@pytest.mark.parametrize("N", STREAM.batches)
+def test_prefill_four_groups_equal_per_group(N):
+    """The four groups' tiles in one launch (largest K first, each group's
+    workgroups a multiple of the XCD count) give exactly the outputs of one
+    prefill launch per group, in every store path and on repeated calls."""
+    ws = W.layer_weights(STREAM, 0)
+    packed = [bt.pack(w.to(DEV), s) for (w, s) in ws]
+    L = bt.Layer(packed, STREAM.shapes)
+    xs = [x.to(DEV) for x in W.layer_inputs(STREAM, 0, N)]
+    for ydt in (bt.BT_BF16, bt.BT_I32, bt.BT_F32, bt.BT_BF16):
+        a = forward_guarded(L, STREAM, xs, N, ydt)
+        b = L.forward(xs, y_dtype=ydt, per_group=True)
+        for p in range(bt.BT_LAYER_PROJ):
+            assert torch.equal(a[p], b[p]), (N, ydt, p)
+
+
 def test_layer_matches_separate_calls():
     wl = SMALL
     N = 17
