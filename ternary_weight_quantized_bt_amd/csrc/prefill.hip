@@ -25,9 +25,14 @@
 //     dequantizes (float32: acc * (s_w * s_a / 127)) to fp32 / bf16, or
 //     writes the int32 sum.
 // The tile order is XCD-aware: workgroups are handed to the eight XCDs
-// round-robin, so workgroup i is mapped to tile (i % 8) * ceil(T / 8) + i / 8
-// of the token-major tile list -- each XCD then works through a contiguous
-// run of tiles that share activation rows, which stay in its L2.
+// round-robin, so workgroup i is mapped to position (i % 8) * ceil(T / 8) +
+// i / 8 of a tile list made of chunks of ceil(ntok / 8) token tiles, each
+// chunk walked row tile by row tile (all of the chunk's token tiles of one
+// row tile, then the next row tile).  An XCD then works through about one
+// chunk: its activation rows stay in its L2, and each weight tile is used by
+// the chunk's token tiles back to back, so it is fetched into that L2 once
+// rather than once per token tile (-4 % time per prefill step together with
+// the epilogue loads hoisted to the tile's start).
 
 #include <algorithm>
 
@@ -99,7 +104,13 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
     for (int64_t j = b;; j += G) {
         const int64_t idx = (j % kXcds) * per_xcd + j / kXcds;
         if (j / kXcds >= per_xcd || idx >= ntiles) break;  // whole workgroup
-        const int64_t tn = idx / mtiles, tm = idx % mtiles;
+        // chunk cc of TCH token tiles (the last may be shorter), row tile
+        // major within it
+        const int64_t TCH = (ntok + kXcds - 1) / kXcds;
+        const int64_t chunk = mtiles * TCH;
+        const int64_t cc = idx / chunk, rr = idx - cc * chunk;
+        const int64_t tcn = min(TCH, ntok - cc * TCH);
+        const int64_t tm = rr / tcn, tn = cc * TCH + rr % tcn;
         const int64_t tok0 = tn * BN;
 
         // This wave's row tiles (clamped to the last tile past the end; their
@@ -141,6 +152,23 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
             return *reinterpret_cast<const v4i *>(stage(st) + (wn * 16 * TG + g * 16 + r) * kRow +
                                                   16 * ((4 * t + h) ^ r));
         };
+
+        // The epilogue's per-token and per-tile factors, loaded now so their
+        // latency hides under the K loop.
+        float xs_pre[TG];
+        int32_t xsum_pre[TG];
+#pragma unroll
+        for (int g = 0; g < TG; ++g) {
+            const int64_t tc = min(tok0 + wn * 16 * TG + g * 16 + r, N - 1);
+            xs_pre[g] = a.xs[tc];
+            xsum_pre[g] = a.xsum[tc];
+        }
+        float s_w[RT];
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
+            s_w[i] = packed_scale(tr.packed, tr.M, K);
+        }
 
         v4i acc[RT][TG];
 #pragma unroll
@@ -217,13 +245,6 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
         // Epilogue: lane (r, h) holds rows 4h..4h+3 of each row tile for token
         // g*16 + r of each group.  Per-row-tile values are wave-uniform; token
         // values are loaded from a clamped index so only the stores branch.
-        float s_w[RT];
-#pragma unroll
-        for (int i = 0; i < RT; ++i) {
-            const TileRef tr = resolve_tile(a, min(tm * BMT + wm * RT + i, total - 1));
-            s_w[i] = packed_scale(tr.packed, tr.M, K);
-        }
-
         // bf16 output with all of the workgroup's row tiles in one projection
         // (every tile but those at a projection boundary or past the end): the
         // results of 16 tokens at a time go through LDS, token-major, and each
@@ -252,9 +273,8 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
 #pragma unroll
                 for (int g = 0; g < TG; ++g) {
                     int8_t *T = (g & 1) ? sB1 : sB0;
-                    const int64_t tc = min(tok0 + g * 16 + r, N - 1);
-                    const float f = token_factor(sw, a.xs[tc]);
-                    const int32_t sub = a.xsum[tc];
+                    const float f = token_factor(sw, xs_pre[g]);
+                    const int32_t sub = xsum_pre[g];
 #pragma unroll
                     for (int i = 0; i < RT; ++i) {
                         const v4i v = acc[i][g];
@@ -284,9 +304,8 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
 #pragma unroll
             for (int g = 0; g < TG; ++g) {
                 const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;
-                const int64_t tc = min(tok, N - 1);
-                const float s_a = a.xs[tc];
-                const int32_t sub = a.xsum[tc];
+                const float s_a = xs_pre[g];
+                const int32_t sub = xsum_pre[g];
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
                     const int64_t t = tm * BMT + wm * RT + i;
