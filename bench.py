@@ -49,7 +49,17 @@ KERNEL_SOURCES = {
     "decode_dot4_kernel": ("gemv.hip", "dot4.hpp", "common.hpp", "group.hpp", "quant.hpp"),
     "decode_mfma_kernel": ("mfma.hip", "common.hpp", "group.hpp"),
     "prefill_kernel": ("prefill.hip", "common.hpp", "group.hpp"),
+    "prefill_multi_kernel": ("prefill.hip", "common.hpp", "group.hpp", "quant.hip", "quant.hpp"),
+    "decode_mfma_multi_kernel": ("mfma.hip", "common.hpp", "group.hpp", "quant.hip", "quant.hpp"),
 }
+# Steps of the prefill extra (at least these many, whatever --steps and
+# --warmup say; multiples of its 20 steps per graph).
+PREFILL_MIN_STEPS, PREFILL_MIN_WARMUP, PREFILL_PER_GRAPH = 200, 2000, 20
+
+
+def prefill_steps(steps, warmup):
+    g = PREFILL_PER_GRAPH
+    return max(steps, PREFILL_MIN_STEPS) // g * g, max(warmup, PREFILL_MIN_WARMUP) // g * g
 
 
 def parse():
@@ -366,10 +376,50 @@ def trace_summary(folder, steps, warmup, layers, out=TRACE_FILE):
     except (OSError, ValueError):
         doc = {}
     doc[name] = entry
+    # The grouped launches of the 8-token stream and of the 2048-token
+    # prefill, each with the quantization launch just before it: the timed
+    # window of each (its first eager step and warm-up replays skipped).
+    all_rows = _trace_rows(folder)
+    psteps, pwarm = prefill_steps(steps, warmup)
+    for key, marker, skip_n, count_n in (
+            ("decode_mfma_multi_kernel", "decode_mfma_multi_kernel<", layers * (1 + warmup),
+             layers * steps),
+            ("prefill_multi_kernel", "prefill_multi_kernel<", 1 + pwarm, psteps)):
+        g = _grouped_window(all_rows, marker, skip_n, count_n)
+        if g is not None:
+            g["kernel_sha"] = kernel_sha(key)
+            doc[key] = g
     with open(out, "w") as f:
         json.dump(doc, f, indent=1)
     print(json.dumps(entry, indent=1))
     return entry
+
+
+def _grouped_window(rows, marker, skip, count):
+    """Mean durations of a grouped product kernel's dispatches [skip, skip +
+    count) (in start order) and of the quantization launch that precedes each
+    one, with the mean gap between the two; None if the trace has fewer."""
+    import statistics
+    idx = [i for i, r in enumerate(rows) if marker in r[0]]
+    if len(idx) < skip + count:
+        return None
+    win = idx[skip:skip + count]
+    prod = [(rows[i][2] - rows[i][1]) / 1e3 for i in win]
+    quant, gap = [], []
+    for i in win:
+        j = i - 1
+        while j >= 0 and "quant_onepass_kernel<" not in rows[j][0]:
+            j -= 1
+        if j >= 0:
+            quant.append((rows[j][2] - rows[j][1]) / 1e3)
+            gap.append((rows[i][1] - rows[j][2]) / 1e3)
+    out = {"kernel_instance": rows[win[0]][0], "timed_dispatches": count,
+           "skipped_dispatches": skip, "mean_us": round(statistics.fmean(prod), 3),
+           "median_us": round(statistics.median(prod), 3), "min_us": round(min(prod), 3)}
+    if quant:
+        out["quant_mean_us"] = round(statistics.fmean(quant), 3)
+        out["quant_to_product_gap_mean_us"] = round(statistics.fmean(gap), 3)
+    return out
 
 
 def read_trace(kernel_name, sha):
@@ -513,20 +563,29 @@ def prefill_extra(steps, warmup, use_graph):
     # blocks), so one replay launch is not charged to every block.  A step is
     # only ~0.15 ms: at least 2000 warm-up steps (~0.3 s) bring the chip to
     # its steady clocks, and at least 200 timed steps average out the noise.
-    per_graph = 20
-    steps = max(steps, 200) // per_graph * per_graph
-    sec, _ = run_steps(m, steps, max(warmup, 2000) // per_graph * per_graph, use_graph,
-                       per_graph=per_graph)
+    steps, pwarm = prefill_steps(steps, warmup)
+    sec, _ = run_steps(m, steps, pwarm, use_graph, per_graph=PREFILL_PER_GRAPH)
     ops = 2 * 2048 * sum(M * K for M, K in wl.shapes)
     kt, launches = kernel_pass(m, steps)
-    per_launch_ops = ops / 4
     res = {
         "workload": wl.name, "tokens": 2048, "ms_per_step": round(sec * 1e3, 4),
         "int8_tops": round(ops / sec / 1e12, 2),
         "frac_of_int8_peak": round(ops / sec / 1e12 / PEAK_INT8_TOPS, 4),
-        "kernel_avg_us": round(kt * 1e6, 2),
-        "kernel_tops": round(per_launch_ops / kt / 1e12, 2),
+        # the four group products as separate launches, back to back, on
+        # inputs quantized beforehand (the step runs them as one launch)
+        "per_group_launches_us": round(4 * kt * 1e6, 2),
+        "per_group_launches_tops": round(ops / (4 * kt) / 1e12, 2),
     }
+    # The step's four-group product launch alone, from a rocprofv3 kernel
+    # trace of this command (timed window), while its sources are unchanged.
+    tr = read_trace("prefill_multi_kernel", kernel_sha("prefill_multi_kernel"))
+    if tr:
+        res["rocprof_product_kernel_us"] = tr["mean_us"]
+        res["rocprof_product_kernel_tops"] = round(ops / (tr["mean_us"] * 1e-6) / 1e12, 2)
+        res["rocprof_product_frac_of_int8_peak"] = round(
+            ops / (tr["mean_us"] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)
+        if "quant_mean_us" in tr:
+            res["rocprof_quant_kernel_us"] = tr["quant_mean_us"]
     del m
     torch.cuda.empty_cache()
     return res
@@ -855,9 +914,20 @@ def main():
             "ms_per_step": round(s8 * 1e3, 4),
             "packed_gb_per_s": round(model.packed_bytes / s8 / 1e9, 2),
             "frac_of_hbm_peak": round(model.packed_bytes / s8 / 1e9 / PEAK_HBM_GBS, 4),
-            "kernel_avg_us": round(k8 * 1e6, 3),
+            # one group's product launch on pre-quantized inputs, averaged
+            # over the four groups (the step runs the four as one launch)
+            "per_group_launch_avg_us": round(k8 * 1e6, 3),
             "int8_tops": round(16 * sum(M * K for M, K in wl.shapes) * layers / s8 / 1e12, 2),
         }
+        tr8 = read_trace("decode_mfma_multi_kernel", kernel_sha("decode_mfma_multi_kernel"))
+        if tr8:
+            e8 = extra["stream70b_8_tokens"]
+            e8["rocprof_product_kernel_us"] = tr8["mean_us"]
+            e8["rocprof_product_frac_of_hbm_peak"] = round(
+                _block_packed_bytes() / (tr8["mean_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            for k in ("quant_mean_us", "quant_to_product_gap_mean_us"):
+                if k in tr8:
+                    e8["rocprof_" + k] = tr8[k]
     packed_bytes_step = model.packed_bytes
     pack = {"seconds": round(model.pack_s, 3),
             "int8_weights_gb_per_s": round(4 * packed_bytes_step / model.pack_s / 1e9, 2)}

@@ -46,3 +46,35 @@ def test_trace_summary_takes_the_timed_window(tmp_path):
     assert abs(e["busy_fraction_of_span"] - layers * steps * 20_000 / span) < 1e-4
     assert json.load(open(out))["layer_dot4_kernel"]["mean_us"] == 20.0
     assert t0 > 0
+
+
+QUANT = "void bt::(anonymous namespace)::quant_onepass_kernel<unsigned short, 8, 128>(bt::QuantJobs)"
+MULTI = "void bt::(anonymous namespace)::prefill_multi_kernel<4, 4, 4, 1, 2>(bt::(anonymous namespace)::MultiArgs)"
+SINGLE = "void bt::(anonymous namespace)::prefill_kernel<4, 4, 4, 1, 2>(bt::GroupArgs, long)"
+
+
+def test_grouped_window_pairs_each_product_with_its_quantization():
+    # 2 skipped steps (quant 5 us, product 100 us), 3 timed steps (quant 7 us,
+    # 2 us gap, product 110 us), then single-group launches that do not count
+    rows, t = [], 0
+    for i in range(5):
+        timed = i >= 2
+        q = 7_000 if timed else 5_000
+        rows.append((QUANT, t, t + q))
+        t += q + (2_000 if timed else 1_000)
+        rows.append((MULTI, t, t + (110_000 if timed else 100_000)))
+        t += 120_000
+    for i in range(4):
+        rows.append((SINGLE, t, t + 30_000))
+        t += 31_000
+    g = bench._grouped_window(rows, "prefill_multi_kernel<", 2, 3)
+    assert g["timed_dispatches"] == 3 and g["skipped_dispatches"] == 2
+    assert g["mean_us"] == g["min_us"] == 110.0
+    assert g["quant_mean_us"] == 7.0
+    assert g["quant_to_product_gap_mean_us"] == 2.0
+    assert bench._grouped_window(rows, "prefill_multi_kernel<", 3, 3) is None
+
+
+def test_prefill_step_counts():
+    assert bench.prefill_steps(20, 50) == (200, 2000)
+    assert bench.prefill_steps(450, 2010) == (440, 2000)
