@@ -84,12 +84,13 @@ def test_small_layer_f32_inputs():
     run_layer(wl, 0, 5, bt.BT_F32)
 
 
-# Row counts give ragged 256-row tiles in every group; three K values.
+# Row counts give ragged 256-row tiles in every group; three K values; 700
+# tokens leave the XCD tile order a short last chunk of token tiles.
 STREAM = W.Workload(
     name="prefill_groups", index=12, description="four groups of different K in one launch",
     shapes=((272, 2304), (48, 2304), (48, 2304), (2304, 1024), (1040, 2304), (1040, 2304),
             (2304, 3328)),
-    layers=1, batches=(128, 257, 1000), x_dtype="bf16", y_dtype="bf16",
+    layers=1, batches=(128, 257, 700, 1000), x_dtype="bf16", y_dtype="bf16",
     weight_dist="p0_0.4", act_dist="student_t4")
 
 
@@ -107,6 +108,12 @@ def test_prefill_four_groups_equal_per_group(N):
         b = L.forward(xs, y_dtype=ydt, per_group=True)
         for p in range(bt.BT_LAYER_PROJ):
             assert torch.equal(a[p], b[p]), (N, ydt, p)
+
+
+def test_prefill_short_last_chunk_against_oracle():
+    # 700 tokens: 11 token tiles in chunks of 2, the last chunk one tile;
+    # exact int32 sums on sampled rows of every projection, bf16 too
+    run_layer(STREAM, 0, 700, (bt.BT_I32, bt.BT_BF16), rows_per_proj=64, seed_rows=700)
 
 
 def test_layer_matches_separate_calls():
