@@ -282,10 +282,10 @@ bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K,
  * end to end in one grid.  This is the GPU form of processing several weight
  * matrices per invocation to cut launch overhead ([I2S] "How I2_S Kernels
  * Process the Format", weight-parallel kernels).  All projections share K;
- * y of projection i is [N, projs[i].M].  The path is chosen from N exactly as
- * bt_layer_forward does (decode kernels below BT_PREFILL_MIN_N tokens, the
- * prefill kernel from there on), so results equal per-projection
- * bt_ternary_gemv / bt_ternary_gemm calls.
+ * y of projection i is [N, projs[i].M].  The path is chosen from N (decode
+ * kernels below BT_PREFILL_MIN_N tokens, the prefill kernel from there on);
+ * both give the same bits, so results equal per-projection bt_ternary_gemv /
+ * bt_ternary_gemm calls.
  * ---------------------------------------------------------------------- */
 #define BT_MAX_GROUP 3
 #define BT_PREFILL_MIN_N 128
@@ -325,7 +325,11 @@ bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
  *     this interface takes.  The workspace is not touched.
  *   - otherwise, from 2 tokens on: one launch that quantizes the four
  *     inputs into the workspace, then one matrix-core launch for all four
- *     groups (decode below BT_PREFILL_MIN_N tokens, prefill from there).
+ *     groups: the decode kernel (weights streamed once per 16 tokens) up to
+ *     5 / 4 / 3 / 2 groups of 16 tokens for blocks of at most 32 / 64 / 128
+ *     MiB / more of packed weights, the prefill kernel (once per 64 tokens)
+ *     beyond that and from BT_PREFILL_MIN_N tokens on (measured crossovers;
+ *     the two give the same bits).
  *   - otherwise (1 token of a block too large for one launch): one decode
  *     launch per group, each quantizing its own input in its prologue where
  *     the row fits (the other inputs are quantized by one launch first).

@@ -406,6 +406,25 @@ bt_status layer_check(const bt_layer *L, const bt_layer_io *io, const char *fn,
     return ok();
 }
 
+// Which kernel runs a block's four groups from 2 tokens on (one launch
+// either way, identical results).  The matrix-core decode streams the
+// weights once per 16-token group -- the repeats come from the last-level
+// cache while the block fits there -- and the prefill kernel once per 64
+// tokens, at a higher fixed cost.  Measured per block at 17..127 tokens
+// (2B- / 7B- / 13B- / 70B-class blocks: 17 / 51 / 79 / 214 MB of packed
+// weights), the decode is the faster up to 5 / 4 / 3 / 2 token groups; e.g.
+// 64 tokens of a 70B-class block: 119 us per block on the prefill kernel
+// against 197 us on the decode.
+static bool four_groups_prefill(int64_t N, int64_t packed_bytes) {
+    if (N >= BT_PREFILL_MIN_N) return true;
+    constexpr int64_t MB = 1 << 20;
+    const int64_t max_groups = packed_bytes <= 32 * MB    ? 5
+                               : packed_bytes <= 64 * MB  ? 4
+                               : packed_bytes <= 128 * MB ? 3
+                                                          : 2;
+    return (N + 15) / 16 > max_groups;
+}
+
 bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspace,
                         size_t workspace_bytes, bt_stream stream, const char *fn) {
     size_t need_bytes = 0;
@@ -521,9 +540,11 @@ bt_status layer_forward(const bt_layer *L, const bt_layer_io *io, void *workspac
     }
     if (quantized && four_groups) {
         // matrix-core decode or prefill: the four groups in one launch
-        const hipError_t e = N < BT_PREFILL_MIN_N
-                                 ? bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s)
-                                 : bt::launch_prefill_groups(groups, BT_LAYER_INPUTS, s);
+        int64_t bytes = 0;
+        for (int p = 0; p < BT_LAYER_PROJ; ++p) bytes += L->M[p] * L->K[p] / 4;
+        const hipError_t e = four_groups_prefill(N, bytes)
+                                 ? bt::launch_prefill_groups(groups, BT_LAYER_INPUTS, s)
+                                 : bt::launch_decode_groups(groups, BT_LAYER_INPUTS, s);
         return e == hipSuccess ? ok() : hip_status(e, fn);
     }
     for (int i = 0; i < BT_LAYER_INPUTS; ++i) {
