@@ -18,12 +18,16 @@
 //   * B (activations): the BN x 256 int8 block is copied global -> LDS with
 //     the direct 16-byte LDS-load instruction (no registers), double
 //     buffered, the next block in flight while the current one is consumed.
+//     Both loads go through buffer resources (the tile's token rows, each
+//     row tile's packed slots): a lane's offset is fixed for the tile and the
+//     block's offset is a scalar, so the K loop does no address arithmetic
+//     on the vector unit (-2 % per prefill step).
 //     Inside a token's 256-byte row, 16-byte chunk c is stored at position
 //     c ^ (token % 16), so the 16 lanes that read one chunk of 16 different
 //     tokens hit 16 different bank groups.
-//   * After the last block the epilogue subtracts the token's code sum and
-//     dequantizes (float32: acc * (s_w * s_a / 127)) to fp32 / bf16, or
-//     writes the int32 sum.
+//   * The accumulators start at minus the token's code sum, so after the
+//     last block they hold the exact sum; the epilogue dequantizes it
+//     (float32: acc * (s_w * s_a / 127)) to fp32 / bf16, or writes it.
 // The tile order is XCD-aware: workgroups are handed to the eight XCDs
 // round-robin, so workgroup i is mapped to position (i % 8) * ceil(T / 8) +
 // i / 8 of a tile list made of chunks of ceil(ntok / 8) token tiles, each
@@ -43,6 +47,23 @@ namespace bt {
 namespace {
 
 constexpr int kXcds = 8;
+
+// Buffer-resource loads, declared by their LLVM intrinsic names (a plain
+// declaration also parses in the compiler's host pass).  A raw buffer load
+// reads base + voffset (per lane) + soffset (scalar) and returns zeros past
+// num_records bytes; the resource is base, stride 0, num_records and the
+// data-format word of gfx9-family raw buffers.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void bt_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void *lds, int size,
+                                   int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ i32x4_t bt_buffer_load_b128(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ __forceinline__ i32x4_t bt_make_rsrc(const void *p, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xFFFF, bytes, 0x00020000};
+}
+
 
 __device__ __forceinline__ v4i unpack_a(uint32_t word) {
     v4i a;
@@ -129,21 +150,35 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
         // direct load covers 4 tokens; lane l fills position l%16 of token l/16
         // with global chunk (l%16) ^ (token % 16).
         v4u ar[S][RT];
+        // The tile's token rows as one buffer resource (its rows only: at most
+        // BN * K < 2^32 bytes), so each direct load is a 32-bit lane offset
+        // fixed for the tile plus the block's column offset in a scalar.
+        const i32x4_t xrs = bt_make_rsrc(a.xq + tok0 * K, (int)(min((int64_t)BN, N - tok0) * K));
+        i32x4_t ars[RT];
+#pragma unroll
+        for (int i = 0; i < RT; ++i) ars[i] = bt_make_rsrc(abase[i], (int)(qb * kTileBytes));
+        int dvoff[kDmaW];
+#pragma unroll
+        for (int i = 0; i < kDmaW; ++i) {
+            const int d = wave * kDmaW + i;   // 1 KiB unit of the block
+            const int tl = d * 4 + lane / 16;  // token within the tile
+            const int64_t tok = min(tok0 + tl, N - 1);
+            const int c = (lane % 16) ^ (tl % 16);
+            dvoff[i] = (int)((tok - tok0) * K + 16 * c);
+        }
         auto issue = [&](int64_t q, int st) {
             q = min(q, qb - 1);
 #pragma unroll
-            for (int i = 0; i < RT; ++i)
-                ar[st][i] = *to_global(reinterpret_cast<const v4u *>(abase[i] + q * kTileBytes) + lane);
+            for (int i = 0; i < RT; ++i) {
+                const i32x4_t v = bt_buffer_load_b128(ars[i], 16 * lane, (int)(q * kTileBytes), 0);
+                ar[st][i] = v4u{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
+            }
 #pragma unroll
             for (int i = 0; i < kDmaW; ++i) {
-                const int d = wave * kDmaW + i;   // 1 KiB unit of the block
-                const int tl = d * 4 + lane / 16;  // token within the tile
-                const int64_t tok = min(tok0 + tl, N - 1);
-                const int c = (lane % 16) ^ (tl % 16);
-                const int8_t *src = a.xq + tok * K + q * kTileCols + 16 * c;
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)src,
-                    (__attribute__((address_space(3))) void *)(stage(st) + d * 1024), 16, 0, 0);
+                const int d = wave * kDmaW + i;
+                bt_buffer_load_lds(
+                    xrs, (__attribute__((address_space(3))) void *)(stage(st) + d * 1024), 16,
+                    dvoff[i], (int)(q * kTileCols), 0, 0);
             }
         };
         // B fragment of token group g, 64-column step t, from stage st: token
@@ -170,11 +205,14 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
             s_w[i] = packed_scale(tr.packed, tr.M, K);
         }
 
+        // Accumulators start at minus the token's code sum, so they end at
+        // sum (code - 1) * xq (exact in int32) with no subtraction after.
         v4i acc[RT][TG];
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
-            for (int g = 0; g < TG; ++g) acc[i][g] = v4i{0, 0, 0, 0};
+            for (int g = 0; g < TG; ++g)
+                acc[i][g] = v4i{-xsum_pre[g], -xsum_pre[g], -xsum_pre[g], -xsum_pre[g]};
 
         // Prologue: blocks 0 .. S-2 in flight.
 #pragma unroll
@@ -274,16 +312,13 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
                 for (int g = 0; g < TG; ++g) {
                     int8_t *T = (g & 1) ? sB1 : sB0;
                     const float f = token_factor(sw, xs_pre[g]);
-                    const int32_t sub = xsum_pre[g];
 #pragma unroll
                     for (int i = 0; i < RT; ++i) {
                         const v4i v = acc[i][g];
                         typedef unsigned v2u __attribute__((ext_vector_type(2)));
                         *reinterpret_cast<v2u *>(T + r * kPitch + 2 * ((wm * RT + i) * kTileRows + 4 * h)) =
-                            v2u{f32x2_to_bf16x2(__fmul_rn((float)(v.x - sub), f),
-                                                __fmul_rn((float)(v.y - sub), f)),
-                                f32x2_to_bf16x2(__fmul_rn((float)(v.z - sub), f),
-                                                __fmul_rn((float)(v.w - sub), f))};
+                            v2u{f32x2_to_bf16x2(__fmul_rn((float)v.x, f), __fmul_rn((float)v.y, f)),
+                                f32x2_to_bf16x2(__fmul_rn((float)v.z, f), __fmul_rn((float)v.w, f))};
                     }
                     __syncthreads();
                     for (int c = (int)threadIdx.x; c < 16 * kPerTok; c += kWaves * kWave) {
@@ -305,7 +340,6 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
             for (int g = 0; g < TG; ++g) {
                 const int64_t tok = tok0 + wn * 16 * TG + g * 16 + r;
                 const float s_a = xs_pre[g];
-                const int32_t sub = xsum_pre[g];
 #pragma unroll
                 for (int i = 0; i < RT; ++i) {
                     const int64_t t = tm * BMT + wm * RT + i;
@@ -313,7 +347,7 @@ __device__ __forceinline__ void prefill_group(const GroupArgs &a, int64_t mtiles
                     const TileRef tr = resolve_tile(a, t);
                     const float f = token_factor(s_w[i], s_a);
                     const int64_t base = tok * tr.M + tr.mt * kTileRows + 4 * h;
-                    if (tok < N) store_out4(tr.y, a.ydt, base, acc[i][g], sub, f);
+                    if (tok < N) store_out4(tr.y, a.ydt, base, acc[i][g], 0, f);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep one token group's values live at a time
             }
