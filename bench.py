@@ -655,7 +655,9 @@ def small_configs_extra(steps, warmup, use_graph):
     import workloads as W
     dev = "cuda:0"
     res = {}
-    # single GEMV: quantize the token, then the product
+    # single GEMV from the float token: bt_ternary_linear (one launch, the
+    # token quantized in the kernel's prologue); beside it the two-call path
+    # (bt_quant_act, then bt_ternary_gemv)
     wl = W.GEMV_2560
     M, K = wl.shapes[0]
     x = W.layer_inputs(wl, 0, 1, dev)[0]
@@ -663,6 +665,7 @@ def small_configs_extra(steps, warmup, use_graph):
     xsc = torch.empty(1, dtype=torch.float32, device=dev)
     xsm = torch.empty(1, dtype=torch.int32, device=dev)
     y = torch.empty((1, M), dtype=torch.float32, device=dev)
+    assert bt.bt_linear_one_launch(1, M, K, bt.BT_F32) == 1
     row = {}
     for name, copies in (("hot", 1), ("cold", 192)):
         ps = [bt.pack(W.ternary_weights(M, K, wl.weight_dist, W.weight_seed(wl, c, 0), dev), 0.02)
@@ -670,14 +673,21 @@ def small_configs_extra(steps, warmup, use_graph):
 
         def step():
             for pk in ps:
+                bt.bt_ternary_linear(pk, M, K, x, bt.BT_F32, 1, y, bt.BT_F32, None, 0)
+
+        def step_two_calls():
+            for pk in ps:
                 bt.bt_quant_act(x, bt.BT_F32, 1, K, xq, xsc, xsm)
                 bt.bt_ternary_gemv(pk, M, K, xq, xsc, xsm, 1, y, bt.BT_F32)
         reps = 20 if copies == 1 else 1
         sec, _ = run_steps(None, steps * reps, warmup * reps, use_graph, step=step,
                            per_graph=reps)
+        sec2, _ = run_steps(None, steps * reps, warmup * reps, use_graph, step=step_two_calls,
+                            per_graph=reps)
         per = sec / copies
         row[name] = {"copies": copies, "us_per_call": round(per * 1e6, 3),
-                     "packed_gb_per_s": round(M * K / 4 / per / 1e9, 1)}
+                     "packed_gb_per_s": round(M * K / 4 / per / 1e9, 1),
+                     "two_calls_us_per_call": round(sec2 / copies * 1e6, 3)}
         del ps
     res["gemv_2560"] = row
     for wl, N in ((W.LAYER2B_N1, 1), (W.LAYER2B_N64, 64)):

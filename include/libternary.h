@@ -28,7 +28,8 @@
  *     no-op.
  *   - Every array argument is a DEVICE pointer, 16-byte aligned, owned by the
  *     caller.  The library never allocates, frees or synchronizes; scratch
- *     space is passed in by the caller (bt_layer_io.workspace), except in
+ *     space is passed in by the caller (bt_layer_io.workspace, the workspace
+ *     arguments of bt_ternary_linear and bt_quantize_weights), except in
  *     bt_layer_forward_noalloc, whose scratch is a static device array.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously on it; results are ready when the stream is.
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define BT_ABI_VERSION 7
+#define BT_ABI_VERSION 8
 #define BT_MAX_K 131840
 #define BT_MAX_N 2097152 /* tokens per call */
 #define BT_TAIL_BYTES 256
@@ -300,6 +301,37 @@ bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
                                   const int8_t *xq, const float *x_scale,
                                   const int32_t *x_sum, int64_t N,
                                   bt_dtype y_dtype, bt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * One projection from float activations: the whole BitLinear forward of
+ * [PARA] section 5 (Quant8 of the input, the ternary product, the rescale by
+ * s_w * x_scale / 127) in one call.  Results are those of bt_quant_act
+ * followed by bt_ternary_gemv (N < BT_PREFILL_MIN_N) or bt_ternary_gemm on
+ * the same tokens, bit for bit.
+ *   x is [N, K] of x_dtype (BT_F32 or BT_BF16), 16-byte aligned; packed, M,
+ *   K, y and y_dtype as for bt_ternary_gemv.
+ *   - Where the decode kernel can quantize the tokens itself
+ *     (bt_linear_one_launch(N, M, K, x_dtype) == 1: 1 token of K up to
+ *     32768 in bf16 or 16384 in fp32, 2..4 tokens of short rows) this is
+ *     ONE launch: every workgroup rounds the tokens into its LDS, nothing
+ *     is written besides y, and the workspace is not touched (it may be
+ *     NULL).
+ *   - Otherwise the codes, scales and sums go through the workspace
+ *     (bt_linear_workspace_bytes(N, K) bytes, 256-byte aligned; a smaller
+ *     or missing one gives BT_ERR_WORKSPACE and launches nothing): one
+ *     quantization launch, then the product.  Its contents after the call
+ *     are unspecified.
+ * ---------------------------------------------------------------------- */
+size_t bt_linear_workspace_bytes(int64_t N, int64_t K);
+
+/* 1 if bt_ternary_linear runs these arguments as one launch, 0 if as two, -1
+ * if they are invalid.  Host-only; no GPU work. */
+int bt_linear_one_launch(int64_t N, int64_t M, int64_t K, bt_dtype x_dtype);
+
+bt_status bt_ternary_linear(const uint8_t *packed, int64_t M, int64_t K,
+                            const void *x, bt_dtype x_dtype, int64_t N,
+                            void *y, bt_dtype y_dtype, void *workspace,
+                            size_t workspace_bytes, bt_stream stream);
 
 /* ------------------------------------------------------------------------
  * Per-layer projection driver.  One transformer block has seven ternary

@@ -84,7 +84,7 @@ BT_WSCALE_ABSMAX = 1
 BT_WQ_WORKSPACE_BYTES = 4096
 
 # The C ABI version these structures and signatures follow (BT_ABI_VERSION).
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lib = None
 
@@ -143,6 +143,12 @@ def lib() -> ctypes.CDLL:
         L.bt_ternary_matmul_group.argtypes = [ctypes.POINTER(bt_proj), S, I64, P, P,
                                               P, I64, S, P]
         L.bt_ternary_matmul_group.restype = S
+        L.bt_linear_workspace_bytes.argtypes = [I64, I64]
+        L.bt_linear_workspace_bytes.restype = ctypes.c_size_t
+        L.bt_linear_one_launch.argtypes = [I64, I64, I64, S]
+        L.bt_linear_one_launch.restype = S
+        L.bt_ternary_linear.argtypes = [P, I64, I64, P, S, I64, P, S, P, ctypes.c_size_t, P]
+        L.bt_ternary_linear.restype = S
         L.bt_layer_one_launch.argtypes = [ctypes.POINTER(bt_layer), I64, S]
         L.bt_layer_one_launch.restype = S
         L.bt_layer_workspace_bytes.argtypes = [ctypes.POINTER(bt_layer), I64]
@@ -298,6 +304,20 @@ def bt_ternary_matmul_group(projs, count, K, xq, x_scale, x_sum, N, y_dtype,
     """projs: a ctypes array of bt_proj (see make_projs)."""
     _check(lib().bt_ternary_matmul_group(projs, count, K, _p(xq), _p(x_scale),
                                          _p(x_sum), N, y_dtype, _stream(stream)))
+
+
+def bt_linear_workspace_bytes(N: int, K: int) -> int:
+    return lib().bt_linear_workspace_bytes(N, K)
+
+
+def bt_linear_one_launch(N: int, M: int, K: int, x_dtype: int) -> int:
+    return lib().bt_linear_one_launch(N, M, K, x_dtype)
+
+
+def bt_ternary_linear(packed, M, K, x, x_dtype, N, y, y_dtype, workspace,
+                      workspace_bytes, stream=None):
+    _check(lib().bt_ternary_linear(_p(packed), M, K, _p(x), x_dtype, N, _p(y), y_dtype,
+                                   _p(workspace), workspace_bytes, _stream(stream)))
 
 
 def make_projs(items):
@@ -463,6 +483,27 @@ def gemv_b3(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None, y=None):
 
 def gemm(packed, M, K, xq, xs, xsum, y_dtype=BT_F32, stream=None, y=None):
     return _matmul(bt_ternary_gemm, packed, M, K, xq, xs, xsum, y_dtype, stream, y)
+
+
+def linear(packed, M, K, x, y_dtype=BT_F32, workspace=None, stream=None, y=None):
+    """float32 / bfloat16 x [N, K] -> y [N, M]: quantization and product in
+    one call (one launch where the decode kernel quantizes the tokens itself,
+    else through a workspace, allocated here unless given)."""
+    N = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K or x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x must be float32 / bfloat16 [N, {K}], got "
+                         f"{tuple(x.shape)} {x.dtype}")
+    _check_packed(packed, bt_packed_bytes(M, K), "linear")
+    y = _out(y, (N, M), _TORCH_DTYPE[y_dtype], x.device, "linear y")
+    xdt = _BT_DTYPE[x.dtype]
+    need = 0 if bt_linear_one_launch(N, M, K, xdt) == 1 else bt_linear_workspace_bytes(N, K)
+    made = None
+    if workspace is None and need:
+        made = workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() if workspace is not None else 0
+    bt_ternary_linear(packed, M, K, x, xdt, N, y, y_dtype, workspace, wbytes, stream)
+    _keep_for_stream((made,), stream)
+    return y
 
 
 class Layer:

@@ -341,6 +341,63 @@ bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K, const int
     return hip_status(bt::launch_prefill(g, as_stream(stream)), fn);
 }
 
+// Workspace of the two-launch linear path: codes [N, K], scales [N], sums [N],
+// each block 256-byte aligned.
+static size_t linear_ws_bytes(int64_t N, int64_t K) {
+    return align256((size_t)N * (size_t)K) + 2 * align256((size_t)N * sizeof(float));
+}
+
+static bool linear_fuses(int64_t N, int64_t M, int64_t K, bt_dtype xdt) {
+    return N < BT_PREFILL_MIN_N && bt::decode_fuses_quant(N, M, K, xdt);
+}
+
+size_t bt_linear_workspace_bytes(int64_t N, int64_t K) {
+    if (N < 0 || N > BT_MAX_N || K <= 0 || K % 256 != 0 || K > BT_MAX_K) return 0;
+    return linear_ws_bytes(N, K);
+}
+
+int bt_linear_one_launch(int64_t N, int64_t M, int64_t K, bt_dtype x_dtype) {
+    if (N < 0 || N > BT_MAX_N || (x_dtype != BT_F32 && x_dtype != BT_BF16)) return -1;
+    if (check_mk(M, K, "bt_linear_one_launch") != BT_OK) return -1;
+    return N > 0 && linear_fuses(N, M, K, x_dtype) ? 1 : 0;
+}
+
+bt_status bt_ternary_linear(const uint8_t *packed, int64_t M, int64_t K, const void *x,
+                            bt_dtype x_dtype, int64_t N, void *y, bt_dtype y_dtype,
+                            void *workspace, size_t workspace_bytes, bt_stream stream) {
+    const char *fn = "bt_ternary_linear";
+    BT_TRY(check_mk(M, K, fn));
+    BT_TRY(check_n(N, fn));
+    if (x_dtype != BT_F32 && x_dtype != BT_BF16)
+        return fail(BT_ERR_DTYPE, "%s: x dtype must be BT_F32 or BT_BF16", fn);
+    if (y_dtype != BT_F32 && y_dtype != BT_BF16 && y_dtype != BT_I32)
+        return fail(BT_ERR_DTYPE, "%s: unsupported y dtype %d", fn, (int)y_dtype);
+    BT_TRY(check_ptr(packed, "packed", fn));
+    if (N == 0) return ok();
+    BT_TRY(check_ptr(x, "x", fn));
+    BT_TRY(check_ptr(y, "y", fn));
+    hipStream_t s = as_stream(stream);
+    if (linear_fuses(N, M, K, x_dtype)) {
+        // one launch: every decode workgroup quantizes the tokens into LDS
+        const bt::Group g = single_group(packed, M, K, nullptr, nullptr, nullptr, N, y, y_dtype);
+        return hip_status(bt::launch_decode_fused(g, x, x_dtype, s), fn);
+    }
+    const size_t need = linear_ws_bytes(N, K);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(BT_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(BT_ERR_ALIGN, "%s: workspace is not 256-byte aligned", fn);
+    uint8_t *b = static_cast<uint8_t *>(workspace);
+    int8_t *xq = reinterpret_cast<int8_t *>(b);
+    float *xs = reinterpret_cast<float *>(b + align256((size_t)N * (size_t)K));
+    int32_t *xsum = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(xs) +
+                                                align256((size_t)N * sizeof(float)));
+    hipError_t e = bt::launch_quant(x, x_dtype, N, K, xq, xs, xsum, s);
+    if (e == hipSuccess) e = run_group(single_group(packed, M, K, xq, xs, xsum, N, y, y_dtype), s);
+    return hip_status(e, fn);
+}
+
 bt_status bt_ternary_matmul_group(const bt_proj *projs, int count, int64_t K,
                                   const int8_t *xq, const float *x_scale,
                                   const int32_t *x_sum, int64_t N, bt_dtype y_dtype,

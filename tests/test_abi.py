@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
               "bt_dequantize_weights", "bt_i2s_import", "bt_i2s_export", "bt_i2s_bytes",
               "bt_b3_bytes", "bt_pack_ternary_b3", "bt_unpack_ternary_b3",
               "bt_ternary_gemv_b3",
-              "bt_ternary_gemv", "bt_ternary_gemm", "bt_layer_forward",
+              "bt_ternary_gemv", "bt_ternary_gemm", "bt_ternary_linear",
+              "bt_linear_workspace_bytes", "bt_linear_one_launch", "bt_layer_forward",
               "bt_layer_workspace_bytes", "bt_layer_forward_noalloc",
               "bt_packed_bytes", "bt_last_error",
               "bt_abi_version"):
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     header = open(os.path.join(ROOT, "include", "libternary.h")).read()
     declared = int(re.search(r"#define BT_ABI_VERSION (\d+)", header).group(1))
-    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 7
+    assert bt.bt_abi_version() == declared == bt.ABI_VERSION == 8
 
 
 def test_packed_bytes():
@@ -288,6 +289,56 @@ def test_layer_one_launch_choice():
     bad = list(LAYER)
     bad[1] = (32, 512)
     assert bt.bt_layer_one_launch(_layer(bad), 1, bt.BT_BF16) == -1
+
+
+def test_linear_workspace_bytes():
+    # codes [N, K], then scales and sums [N], each 256-byte aligned
+    assert bt.bt_linear_workspace_bytes(8, 2560) == 20480 + 256 + 256
+    assert bt.bt_linear_workspace_bytes(2048, 6912) == 2048 * 6912 + 8192 + 8192
+    assert bt.bt_linear_workspace_bytes(3, 256) == 768 + 256 + 256
+    assert bt.bt_linear_workspace_bytes(0, 256) == 0 + 0 + 0
+    assert bt.bt_linear_workspace_bytes(-1, 256) == 0
+    assert bt.bt_linear_workspace_bytes(1, 300) == 0
+
+
+def test_linear_one_launch_choice():
+    F, B = bt.BT_F32, bt.BT_BF16
+    assert bt.bt_linear_one_launch(1, 2560, 2560, F) == 1
+    assert bt.bt_linear_one_launch(1, 48, 32768, B) == 1    # 8 chunks per thread
+    assert bt.bt_linear_one_launch(1, 48, 33024, B) == 0
+    assert bt.bt_linear_one_launch(1, 48, 16384, F) == 1
+    assert bt.bt_linear_one_launch(1, 48, 16640, F) == 0
+    assert bt.bt_linear_one_launch(3, 208, 2304, B) == 1
+    assert bt.bt_linear_one_launch(8, 4096, 2560, B) == 0   # matrix-core decode
+    assert bt.bt_linear_one_launch(200, 64, 2560, B) == 0   # prefill
+    assert bt.bt_linear_one_launch(0, 64, 2560, B) == 0
+    assert bt.bt_linear_one_launch(1, 15, 2560, B) == -1
+    assert bt.bt_linear_one_launch(1, 16, 2560, bt.BT_I32) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 16, 256, A, bt.BT_I32, 1, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_DTYPE),
+    ((A, 16, 256, A, bt.BT_F32, 1, A, 9, A, 1 << 20), bt.BT_ERR_DTYPE),
+    ((A, 16, 300, A, bt.BT_F32, 1, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_SHAPE),
+    ((A, 16, 256, A, bt.BT_F32, -2, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_INVALID_ARG),
+    ((None, 16, 256, A, bt.BT_F32, 1, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, None, bt.BT_F32, 1, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_INVALID_ARG),
+    ((A, 16, 256, A + 4, bt.BT_F32, 1, A, bt.BT_F32, A, 1 << 20), bt.BT_ERR_ALIGN),
+    ((A, 16, 256, A, bt.BT_F32, 1, A + 2, bt.BT_F32, A, 1 << 20), bt.BT_ERR_ALIGN),
+    # through the workspace (8 tokens of a 4096-row matrix): missing, short,
+    # misaligned -- all refused before anything is launched
+    ((A, 4096, 2560, A, bt.BT_BF16, 8, A, bt.BT_F32, None, 0), bt.BT_ERR_WORKSPACE),
+    ((A, 4096, 2560, A, bt.BT_BF16, 8, A, bt.BT_F32, A, 20991), bt.BT_ERR_WORKSPACE),
+    ((A, 4096, 2560, A, bt.BT_BF16, 8, A, bt.BT_F32, A + 16, 1 << 20), bt.BT_ERR_ALIGN),
+])
+def test_linear_validation(args, status):
+    with pytest.raises(bt.BtError) as e:
+        bt.bt_ternary_linear(*args, stream=0)
+    assert e.value.status == status
+
+
+def test_linear_empty_batch_is_a_noop():
+    bt.bt_ternary_linear(A, 16, 256, None, bt.BT_BF16, 0, None, bt.BT_F32, None, 0, stream=0)
 
 
 def test_binding_refuses_cpu_tensors():
