@@ -112,6 +112,49 @@ struct Chunk<uint16_t> {
         return e;
     }
 };
+// The kernel's view of the 32-bit bookkeeping words of LayerArgs (tend32
+// through scount) held one per lane of a register (field[i] is a readlane
+// with a scalar lane index), with the weight and output pointers in the
+// register's upper lanes.  LayerSched reads it as it reads LayerArgs.
+struct LaneWords {
+    uint32_t v;
+    int base;
+    __device__ int operator[](int i) const { return (int)__builtin_amdgcn_readlane(v, base + i); }
+};
+struct BookView {
+    LaneWords tend32, gend32, k32, xoff32, qb32, heavy, sstart, scount;
+    int sched, n0, ts;
+    __device__ explicit BookView(uint32_t v)
+        : tend32{v, 0}, gend32{v, 7}, k32{v, 11}, xoff32{v, 15}, qb32{v, 19}, heavy{v, 26},
+          sstart{v, 28}, scount{v, 30}, sched((int)__builtin_amdgcn_readlane(v, 23)),
+          n0((int)__builtin_amdgcn_readlane(v, 24)), ts((int)__builtin_amdgcn_readlane(v, 25)) {}
+    // Lanes 32..59 hold the first 28 words of LayerArgs: packed[7], then y[7].
+    __device__ uint64_t word2(int i) const {
+        return (uint64_t)(uint32_t)tend32[32 + i] | ((uint64_t)(uint32_t)tend32[33 + i] << 32);
+    }
+    __device__ const uint8_t *packed(int p) const {
+        return reinterpret_cast<const uint8_t *>(word2(2 * p));
+    }
+    __device__ void *y(int p) const { return reinterpret_cast<void *>(word2(14 + 2 * p)); }
+    // Rows of projection p, from the tile prefix sums.
+    __device__ int64_t rows(int p) const {
+        return (int64_t)(tend32[p] - (p > 0 ? tend32[p - 1] : 0)) * kTileRows;
+    }
+};
+static_assert(offsetof(LayerArgs, packed) == 0 && offsetof(LayerArgs, y) == 56,
+              "pointer words");
+static_assert(offsetof(LayerArgs, gend32) - offsetof(LayerArgs, tend32) == 4 * 7 &&
+                  offsetof(LayerArgs, k32) - offsetof(LayerArgs, tend32) == 4 * 11 &&
+                  offsetof(LayerArgs, xoff32) - offsetof(LayerArgs, tend32) == 4 * 15 &&
+                  offsetof(LayerArgs, qb32) - offsetof(LayerArgs, tend32) == 4 * 19 &&
+                  offsetof(LayerArgs, sched) - offsetof(LayerArgs, tend32) == 4 * 23 &&
+                  offsetof(LayerArgs, n0) - offsetof(LayerArgs, tend32) == 4 * 24 &&
+                  offsetof(LayerArgs, ts) - offsetof(LayerArgs, tend32) == 4 * 25 &&
+                  offsetof(LayerArgs, heavy) - offsetof(LayerArgs, tend32) == 4 * 26 &&
+                  offsetof(LayerArgs, sstart) - offsetof(LayerArgs, tend32) == 4 * 28 &&
+                  offsetof(LayerArgs, scount) - offsetof(LayerArgs, tend32) == 4 * 30,
+              "bookkeeping word positions");
+
 // B3: the weights are base-3 B3T1024 tiles (16 rows x 1024 columns, base3.hpp)
 // instead of T16Q256 ones; a K split part is then a 1024-column tile column.
 template <typename T, int NT, int WAVES, int P, int RING, bool B3>
@@ -160,6 +203,24 @@ void layer_dot4_kernel(LayerArgs a) {
                      "s"(wt[10]), "s"(wt[11]), "s"(wt[12]), "s"(wt[13]), "s"(wt[14]),
                      "s"(wt[15]));
     }
+    // The schedule's 32-bit words (tend32 .. scount) in lanes 0..31 and the
+    // weight and output pointers (packed[], y[]) in lanes 32..59 of one
+    // register, by ONE vector load issued ahead of the input loads; every
+    // lookup is then a readlane with a scalar index.  Read through the scalar
+    // cache, the setup's lookups were chains of dependent loads, each waited
+    // for, in all 16 waves of the unit: the first barrier came 2.1 us after
+    // the input loads went out, and a 2560/6912 block at one token took
+    // 11.95 us against 11.56 us now (70B-class: 0.2 % in alternating runs).
+    static_assert(offsetof(LayerArgs, scount) + 8 - offsetof(LayerArgs, tend32) == 4 * 32,
+                  "32 bookkeeping words");
+    uint32_t bkv;
+    {
+        const auto *k0 = reinterpret_cast<const uint32_t *>(
+            reinterpret_cast<uintptr_t>(__builtin_amdgcn_kernarg_segment_ptr()));
+        const auto *kb = k0 + offsetof(LayerArgs, tend32) / 4;
+        bkv = *to_global(lane < 32 ? kb + lane : k0 + min(lane - 32, 27));
+    }
+    const BookView bk(bkv);
     const int h = lane / 16;
     const int nvalid = (int)min((int64_t)NT, a.N);
     const int kpart = wave % P, sub = wave / P;
@@ -226,36 +287,36 @@ void layer_dot4_kernel(LayerArgs a) {
 
     // Tile bookkeeping in 32-bit scalars: tile and slot counts are far below
     // 2^31, and 64-bit compares would run on the vector unit.
-    const int total = a.tend32[kLayerProj - 1];
+    const int total = bk.tend32[kLayerProj - 1];
     // This workgroup's tile groups (see LayerArgs::sched and LayerSched): nS
     // light ones from sfirst, then nB heavy ones from bfirst; or every G-th
     // from w.
     const int G = (int)gridDim.x, w = (int)blockIdx.x;
-    const LayerSched ls(a, w, G, TPW);
+    const LayerSched ls(bk, w, G, TPW);
     const int nit = ls.nit;
     auto group_of = [&](int it) { return ls.group_of(it); };
     auto tile_of = [&](int it) { return group_of(it) * TPW + sub; };
     // This wave's blocks in a tile of input group g: kpart, kpart + P, ...
     // (interleaved, so the waves of a tile read neighbouring KiB together),
     // nq(g) of them, at least one (K >= 256 * P).
-    auto nq = [&](int g) { return (sel(a.qb32, g) - kpart + P - 1) / P; };
+    auto nq = [&](int g) { return (bk.qb32[g] - kpart + P - 1) / P; };
     // Projection of a tile index that only grows (each cursor below walks
     // its tiles in order): re-resolved only when the tile leaves the current
     // projection's tile range [start, end).
     struct Win {
         int p, start, end;
     };
-    auto win0 = [&]() { return Win{0, 0, a.tend32[0]}; };
+    auto win0 = [&]() { return Win{0, 0, bk.tend32[0]}; };
     auto seek = [&](Win &w, int t) {
         while (t >= w.end) {
             ++w.p;
             w.start = w.end;
-            w.end = sel(a.tend32, w.p);
+            w.end = bk.tend32[w.p];
         }
     };
 
     // Slots of this wave: nq(g) per tile of input group g among its tiles.
-    const int nslots = ls.slots(a, sub, kpart, P);
+    const int nslots = ls.slots(bk, sub, kpart, P);
     const bool has_work = nit > 0 && tile_of(0) < total;
 
     // Load cursor: tile iteration lit, lrem slots left in its tile (the
@@ -272,8 +333,8 @@ void layer_dot4_kernel(LayerArgs a) {
             seek(lw, t);
             const int g = proj_group(lw.p);
             lnq = nq(g);
-            lqb = sel(a.qb32, g);
-            lbase = sel(a.packed, lw.p);
+            lqb = bk.qb32[g];
+            lbase = bk.packed(lw.p);
         }
         lrem = lnq;
         if constexpr (B3)
@@ -446,8 +507,8 @@ void layer_dot4_kernel(LayerArgs a) {
             seek(cw, t);
             const int g = proj_group(cw.p);
             cnq = nq(g);
-            cK = sel(a.k32, g);
-            xb = codes + sel(a.xoff32, g) + (B3 ? 256 : 16) * h;
+            cK = bk.k32[g];
+            xb = codes + bk.xoff32[g] + (B3 ? 256 : 16) * h;
             cfirst = false;
         }
         cq = kpart;
@@ -496,9 +557,9 @@ void layer_dot4_kernel(LayerArgs a) {
                     int t = 0;
 #pragma unroll
                     for (int q = 0; q < P; ++q) t += red[buf][s * P + q][j][r];
-                    const int64_t M = sel(a.M, p);
+                    const int64_t M = bk.rows(p);
                     const float f = token_factor(s_ws[p], __uint_as_float(s_amax[g * NT + j]));
-                    store_out(sel(a.y, p), a.ydt, j * M + (int64_t)(tile - ow.start) * kTileRows + r,
+                    store_out(bk.y(p), a.ydt, j * M + (int64_t)(tile - ow.start) * kTileRows + r,
                               t - (int32_t)s_sum[g * NT + j], f);
                 }
             }

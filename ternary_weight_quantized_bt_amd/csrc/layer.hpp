@@ -79,14 +79,16 @@ struct LayerArgs {
 };
 
 // One workgroup's work under a LayerArgs schedule, shared by the kernel and
-// the host-side schedule tests (so they check exactly what the kernel runs):
+// the host-side schedule tests (so they check exactly what the kernel runs;
+// the kernel passes a register view of the same fields, the host LayerArgs):
 // nit iterations; in iteration it, sub-group s (of tpw) takes the row tile
 // tile_for(it, s) (nothing if it is past the last tile), its waves splitting
 // the tile's K blocks.
 struct LayerSched {
     int nS, sfirst, nB, bfirst, nit, w, G, sched, tpw;
 
-    __host__ __device__ LayerSched(const LayerArgs &a, int w_, int G_, int tpw_)
+    template <class A>
+    __host__ __device__ LayerSched(const A &a, int w_, int G_, int tpw_)
         : nS(0), sfirst(0), nB(0), bfirst(0), nit(0), w(w_), G(G_), sched(a.sched), tpw(tpw_) {
         if (sched) {
             // nS light tile groups from sfirst, then nB heavy ones from bfirst
@@ -110,18 +112,21 @@ struct LayerSched {
     __host__ __device__ int tile_for(int it, int s) const { return group_of(it) * tpw + s; }
     // K blocks of a tile of input group g (256-column blocks, or 1024-column
     // base-3 tile columns), and a wave's share kp, kp + P, ... of them.
-    __host__ __device__ static int blocks(const LayerArgs &a, int g) {
+    template <class A>
+    __host__ __device__ static int blocks(const A &a, int g) {
         int q = a.qb32[0];
 #pragma unroll
         for (int k = 1; k < kLayerInputs; ++k) q = g == k ? a.qb32[k] : q;
         return q;
     }
-    __host__ __device__ static int nq(const LayerArgs &a, int g, int kp, int P) {
+    template <class A>
+    __host__ __device__ static int nq(const A &a, int g, int kp, int P) {
         return (blocks(a, g) - kp + P - 1) / P;
     }
     // Slots (blocks) that the wave with K part kpart of sub-group sub streams
     // over all its iterations, per input group in closed form.
-    __host__ __device__ int slots(const LayerArgs &a, int sub, int kpart, int P) const {
+    template <class A>
+    __host__ __device__ int slots(const A &a, int sub, int kpart, int P) const {
         int n = 0;
         if (sched) {
             // tiles tg * tpw + sub for tile groups tg in [g0, g1), per input group
