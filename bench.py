@@ -398,7 +398,8 @@ def trace_summary(folder, steps, warmup, layers, out=TRACE_FILE):
 def _grouped_window(rows, marker, skip, count):
     """Mean durations of a grouped product kernel's dispatches [skip, skip +
     count) (in start order) and of the quantization launch that precedes each
-    one, with the mean gap between the two; None if the trace has fewer."""
+    one, with the mean and median gap between the two; None if the trace has
+    fewer."""
     import statistics
     idx = [i for i, r in enumerate(rows) if marker in r[0]]
     if len(idx) < skip + count:
@@ -419,6 +420,9 @@ def _grouped_window(rows, marker, skip, count):
     if quant:
         out["quant_mean_us"] = round(statistics.fmean(quant), 3)
         out["quant_to_product_gap_mean_us"] = round(statistics.fmean(gap), 3)
+        # the tracer's timestamps occasionally pair a product with an
+        # overlapping or distant quantization record; the median is robust
+        out["quant_to_product_gap_median_us"] = round(statistics.median(gap), 3)
     return out
 
 
@@ -935,7 +939,8 @@ def main():
             e8["rocprof_product_kernel_us"] = tr8["mean_us"]
             e8["rocprof_product_frac_of_hbm_peak"] = round(
                 _block_packed_bytes() / (tr8["mean_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
-            for k in ("quant_mean_us", "quant_to_product_gap_mean_us"):
+            for k in ("quant_mean_us", "quant_to_product_gap_mean_us",
+                      "quant_to_product_gap_median_us"):
                 if k in tr8:
                     e8["rocprof_" + k] = tr8[k]
     packed_bytes_step = model.packed_bytes

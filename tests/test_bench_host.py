@@ -72,6 +72,7 @@ def test_grouped_window_pairs_each_product_with_its_quantization():
     assert g["mean_us"] == g["min_us"] == 110.0
     assert g["quant_mean_us"] == 7.0
     assert g["quant_to_product_gap_mean_us"] == 2.0
+    assert g["quant_to_product_gap_median_us"] == 2.0
     assert bench._grouped_window(rows, "prefill_multi_kernel<", 3, 3) is None
 
 
