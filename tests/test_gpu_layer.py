@@ -256,12 +256,13 @@ def test_base3_layer_per_group(N):
 
 
 def test_base3_layer_shortest_one_launch_rows():
-    # K = 4096 everywhere: one tile column per wave of the K split
+    # K = 4096 everywhere: one tile column per wave of the K split; 3 and 4
+    # tokens also fit one launch here (the four-token instantiation)
     wl = W.Workload(**{**B3_BLOCK.__dict__, "name": "b3_4096",
                        "shapes": ((64, 4096), (16, 4096), (16, 4096), (48, 4096),
                                   (80, 4096), (80, 4096), (32, 4096))})
-    for N in (1, 2):
-        run_layer_b3(wl, 0, N, bt.BT_BF16)
+    for N in (1, 2, 3, 4):
+        run_layer_b3(wl, 0, N, (bt.BT_I32, bt.BT_BF16))
 
 
 def test_base3_layer_short_rows():
