@@ -265,7 +265,8 @@ bt_status bt_quant_act(const void *x, bt_dtype x_dtype, int64_t N, int64_t K,
  * int8 activations -- on the int8 matrix cores from 5 tokens, and from 2
  * tokens where the matrix is tall (M >= 4096) or its rows long);
  * bt_ternary_gemm is the prefill path (many tokens: tiled int8 matrix-core
- * product).  Both accept any N >= 0 and return identical results.
+ * product).  Both accept any N >= 0 and return identical results (gemv
+ * hands more than 65535 * 16 tokens to the prefill kernel).
  * ---------------------------------------------------------------------- */
 bt_status bt_ternary_gemv(const uint8_t *packed, int64_t M, int64_t K,
                           const int8_t *xq, const float *x_scale,

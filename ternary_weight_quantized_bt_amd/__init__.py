@@ -37,6 +37,7 @@ BT_F32 = 0
 BT_BF16 = 1
 BT_I32 = 2
 BT_MAX_K = 131840
+BT_MAX_N = 2097152  # tokens per call
 BT_LAYER_PROJ = 7
 BT_LAYER_INPUTS = 4
 

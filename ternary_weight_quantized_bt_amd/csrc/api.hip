@@ -328,7 +328,10 @@ bt_status bt_ternary_gemv(const uint8_t *packed, int64_t M, int64_t K, const int
     BT_TRY(check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, y, y_dtype));
     if (N == 0) return ok();
     const bt::Group g = single_group(packed, M, K, xq, x_scale, x_sum, N, y, y_dtype);
-    return hip_status(bt::launch_decode(g, as_stream(stream)), fn);
+    // more tokens than the decode grid holds: the prefill kernel (same bits)
+    return hip_status(N > bt::kDecodeMaxN ? bt::launch_prefill(g, as_stream(stream))
+                                          : bt::launch_decode(g, as_stream(stream)),
+                      fn);
 }
 
 bt_status bt_ternary_gemm(const uint8_t *packed, int64_t M, int64_t K, const int8_t *xq,

@@ -95,6 +95,9 @@ int device_cus();
 
 // Largest N for which launch_decode may use the dot4 kernel.
 constexpr int64_t kDot4MaxN = 4;
+// Largest N launch_decode takes: the matrix-core decode lays its 16-token
+// groups along the grid's y axis, at most 65535 of them.
+constexpr int64_t kDecodeMaxN = 65535 * 16;
 
 // The per-layer driver behind bt_layer_forward with its scratch passed
 // explicitly (`fn` names the entry point in error messages), and its argument

@@ -382,6 +382,7 @@ bool fit_plan(const GroupArgs &a, Plan &p, int64_t &grid, int64_t avail) {
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     if (a.N <= 0 || group_tiles(a) == 0) return hipSuccess;
+    if (a.N > kDecodeMaxN) return hipErrorInvalidConfiguration;  // grid y
     static const int64_t stat = static_lds(decode_mfma_kernel<kMfWaves, kMfSplit, kMfRing>);
     if (stat < 0) return hipErrorInvalidDeviceFunction;
     Plan p = plan_group(a);
@@ -401,6 +402,7 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
     for (int i = 0; i < count; ++i) gs[i] = make_group_args(groups[i]);
     const int64_t N = gs[0].N;
     if (N <= 0) return hipSuccess;
+    if (N > kDecodeMaxN) return hipErrorInvalidConfiguration;  // grid y
     Plan p[kMaxMulti];
     int64_t bytes[kMaxMulti], total = 0, codes_max = 0;
     for (int i = 0; i < count; ++i) {

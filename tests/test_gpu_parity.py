@@ -283,6 +283,35 @@ def test_largest_k_exact():
         assert_rel_close(y, ref["y"], 1e-6, "max K float")
 
 
+def test_largest_n_sampled_tokens():
+    """BT_MAX_N tokens of a 256-wide bf16 input (1 GiB) through quant_act and
+    both products: exact codes, scales, sums and int32 sums on sampled tokens
+    (the first and last 16 and 48 random ones), computed by the oracle from
+    those tokens' rows alone (quantization is per token)."""
+    N, M, K = bt.BT_MAX_N, 32, 256
+    print(f"largest N: N={N} M={M} K={K}", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2 ** 21 + 7)
+    x = torch.randn((N, K), generator=g, device=DEV).to(torch.bfloat16)
+    w = _w(M, K, 2121)
+    packed = bt.pack(w.to(DEV), 0.0125)
+    ref_packed, _ = oracle.pack(w.numpy(), 0.0125)
+    xq, xs, xsum = bt.quant_act(x)
+    rng = np.random.default_rng(2121)
+    tok = np.unique(np.r_[np.arange(16), np.arange(N - 16, N), rng.choice(N, 48, replace=False)])
+    idx = torch.from_numpy(tok).to(DEV)
+    rq, rs, rsum = oracle.quant_act(x_for_oracle(x[idx]))
+    assert_equal(to_np(xq[idx]), rq, "codes")
+    assert_equal(to_np(xs[idx]), rs, "scales")
+    assert_equal(to_np(xsum[idx]), rsum, "code sums")
+    acc_ref = oracle.matmul_i32(ref_packed, M, K, rq)
+    for fn in (bt.gemv, bt.gemm):
+        acc = fn(packed, M, K, xq, xs, xsum, bt.BT_I32)
+        assert acc.shape == (N, M)
+        assert_equal(to_np(acc[idx]), acc_ref, f"{fn.__name__} int32 at N={N}")
+        del acc
+
+
 def test_empty_batch_with_real_buffers():
     M, K = 16, 256
     packed = bt.pack(torch.zeros((M, K), dtype=torch.int8, device=DEV), 1.0)
