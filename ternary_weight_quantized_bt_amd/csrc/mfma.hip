@@ -378,6 +378,45 @@ bool fit_plan(const GroupArgs &a, Plan &p, int64_t &grid, int64_t avail) {
     return false;
 }
 
+// The grid of a four-group launch split over the groups (they run side by
+// side and should end together): shares in proportion to each group's weight
+// bytes, rounded by largest remainders so that they add up to `budget` (the
+// workgroups resident at once; one more would wait for a free unit and end a
+// whole workgroup's time late), at most one workgroup per tile group.  With
+// a single 16-token group, a group that runs in K phases counts 1.3 times
+// its bytes: each phase restages the codes and refills the weight ring, and
+// the 70B-class down projection (two phases at 8 tokens) then ends closer to
+// the others.  Measured against equal weighting in alternating runs: 8 70B-
+// class blocks at 8 tokens 0.3544 vs 0.3598 ms (1.1 / 1.2 / 1.3 / 1.4 / 1.6
+// in another sweep: 1.2 / 1.8 / 2.3 / -0.4 / -0.5 % faster), a 7B-class block
+// at 16 tokens 16 % faster, 70B-class at 2 tokens, 13B- and 34B-class at 8-16
+// tokens equal or up to 0.3 % faster; with more token groups it helped some
+// shapes and cost others up to 6 %, so it is left out there.
+void split_grid(const Plan *p, const int64_t *bytes, int count, int64_t budget, int64_t tgroups,
+                int64_t *share) {
+    double w[kMaxMulti], rem[kMaxMulti], wsum = 0;
+    for (int i = 0; i < count; ++i) {
+        w[i] = (double)bytes[i] * (tgroups == 1 && p[i].nph > 1 ? 1.3 : 1.0);
+        wsum += w[i];
+    }
+    int64_t used = 0;
+    for (int i = 0; i < count; ++i) {
+        const double q = (double)budget * w[i] / wsum;
+        share[i] = max((int64_t)1, min(p[i].groups, (int64_t)q));
+        rem[i] = q - (double)(int64_t)q;
+        used += share[i];
+    }
+    while (used < budget) {
+        int best = -1;
+        for (int i = 0; i < count; ++i)
+            if (rem[i] >= 0 && share[i] < p[i].groups && (best < 0 || rem[i] > rem[best])) best = i;
+        if (best < 0) break;
+        ++share[best];
+        rem[best] = -1;
+        ++used;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
@@ -423,11 +462,17 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
     int64_t grid[kMaxMulti] = {};
     int64_t shmem = 0;
     for (int pass = 0; pass < 2; ++pass) {
-        const int64_t budget = max((int64_t)1, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups);
+        // (rounded down, so that all token groups' workgroups are resident at
+        // once: with 3 token groups, 86 per group put two workgroups of 258
+        // into a second round -- 33 tokens of the 2B-style block 0.373 vs
+        // 0.312 ms per 16 blocks, 48 of a 13B-class block 0.624 vs 0.427 ms
+        // per 8)
+        const int64_t budget = max((int64_t)1, (int64_t)device_cus() * per_cu / tgroups);
         shmem = 0;
+        int64_t share[kMaxMulti];
+        split_grid(p, bytes, count, budget, tgroups, share);
         for (int i = 0; i < count; ++i) {
-            const int64_t share = (budget * bytes[i] + total / 2) / total;
-            grid[i] = max((int64_t)1, min(p[i].groups, share));
+            grid[i] = max((int64_t)1, min(p[i].groups, share[i]));
             if (!fit_plan(gs[i], p[i], grid[i], kLdsPerCu - stat)) return hipErrorInvalidConfiguration;
             shmem = max(shmem, p[i].codes + partial_bytes(p[i], grid[i]));
         }
