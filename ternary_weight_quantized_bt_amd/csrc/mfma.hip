@@ -427,7 +427,7 @@ hipError_t launch_mfma_decode(const GroupArgs &a, hipStream_t s) {
     Plan p = plan_group(a);
     const int64_t tgroups = (a.N + 15) / 16;
     const int per_cu = (int)max((int64_t)1, min((int64_t)2, kLdsPerCu / (p.codes + stat)));
-    int64_t grid = max((int64_t)1, min(p.groups, ((int64_t)device_cus() * per_cu + tgroups - 1) / tgroups));
+    int64_t grid = max((int64_t)1, min(p.groups, (int64_t)device_cus() * per_cu / tgroups));
     if (!fit_plan(a, p, grid, kLdsPerCu - stat)) return hipErrorInvalidConfiguration;
     return launch_mf(a, (int)p.nph, (int)p.qph, grid, (size_t)(p.codes + partial_bytes(p, grid)), s);
 }
