@@ -359,7 +359,7 @@ bt_status bt_ternary_linear(const uint8_t *packed, int64_t M, int64_t K,
  *   - otherwise, from 2 tokens on: one launch that quantizes the four
  *     inputs into the workspace, then one matrix-core launch for all four
  *     groups: the decode kernel (weights streamed once per 16 tokens) up to
- *     5 / 4 / 3 / 2 groups of 16 tokens for blocks of at most 32 / 64 / 128
+ *     6 / 4 / 3 / 2 groups of 16 tokens for blocks of at most 32 / 64 / 128
  *     MiB / more of packed weights, the prefill kernel (once per 64 tokens)
  *     beyond that and from BT_PREFILL_MIN_N tokens on (measured crossovers;
  *     the two give the same bits).

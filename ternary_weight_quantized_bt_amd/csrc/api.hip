@@ -472,13 +472,15 @@ bt_status layer_check(const bt_layer *L, const bt_layer_io *io, const char *fn,
 // cache while the block fits there -- and the prefill kernel once per 64
 // tokens, at a higher fixed cost.  Measured per block at 17..127 tokens
 // (2B- / 7B- / 13B- / 70B-class blocks: 17 / 51 / 79 / 214 MB of packed
-// weights), the decode is the faster up to 5 / 4 / 3 / 2 token groups; e.g.
-// 64 tokens of a 70B-class block: 119 us per block on the prefill kernel
-// against 197 us on the decode.
+// weights), the decode is the faster up to 6 / 4 / 3 / 2 token groups; e.g.
+// 64 tokens of a 70B-class block: 117 us per block on the prefill kernel
+// against 195 us on the decode, 96 tokens of 2B-style blocks 31.3 vs 34.1 us
+// (at 7 groups the decode wins on blocks streamed from HBM and loses on one
+// hot block; from 8 groups the prefill kernel wins).
 static bool four_groups_prefill(int64_t N, int64_t packed_bytes) {
     if (N >= BT_PREFILL_MIN_N) return true;
     constexpr int64_t MB = 1 << 20;
-    const int64_t max_groups = packed_bytes <= 32 * MB    ? 5
+    const int64_t max_groups = packed_bytes <= 32 * MB    ? 6
                                : packed_bytes <= 64 * MB  ? 4
                                : packed_bytes <= 128 * MB ? 3
                                                           : 2;
