@@ -21,7 +21,7 @@ SMALL = W.Workload(
     name="small_layer", index=9, description="small block with every kind of tail",
     shapes=((256, 512), (64, 512), (64, 512), (512, 256), (336, 512),
             (336, 512), (512, 1280)),
-    layers=1, batches=(1, 3, 8, 64, 90, 200), x_dtype="bf16", y_dtype="bf16",
+    layers=1, batches=(1, 3, 8, 40, 64, 72, 90, 200), x_dtype="bf16", y_dtype="bf16",
     weight_dist="p0_0.4", act_dist="normal", outlier_frac=0.01, outlier_scale=20.0)
 
 
