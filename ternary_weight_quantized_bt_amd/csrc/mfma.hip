@@ -81,7 +81,9 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0
 // the next, and the last phase dequantizes and stores.
 // One group's work; the workgroup is number bx of the gx that run this group
 // (blockIdx.x and gridDim.x of a launch for this group alone).
-template <int WAVES, int P, int RING>
+// TL: the weight slots are read with ordinary (cached) loads instead of
+// non-temporal ones.
+template <int WAVES, int P, int RING, bool TL = false>
 __device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph, int64_t bx,
                                            int64_t gx) {
     static_assert(WAVES % P == 0, "K split must divide the waves");
@@ -196,7 +198,7 @@ __device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph,
         v4u ring[kSlots];
 #pragma unroll
         for (int d = 0; d < RING; ++d) {
-            ring[d] = __builtin_nontemporal_load(lp);
+            ring[d] = (TL ? *lp : __builtin_nontemporal_load(lp));
             advance_load();
         }
         // Everything but the ring is complete and visible after this.
@@ -261,7 +263,7 @@ __device__ __forceinline__ void mfma_group(const GroupArgs &a, int nph, int qph,
                         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_a(words[t]), B, acc, 0, 0, 0);
                     }
                 }
-                ring[(d + RING) % kSlots] = __builtin_nontemporal_load(lp);
+                ring[(d + RING) % kSlots] = (TL ? *lp : __builtin_nontemporal_load(lp));
                 advance_load();
                 if (i < nslots && ++cq == q1) {
                     iter_done(cit);
@@ -290,18 +292,18 @@ struct MultiArgs {
     int start[kMaxMulti + 1];  // unused groups have empty ranges
 };
 
-template <int WAVES, int P, int RING>
+template <int WAVES, int P, int RING, bool TL = false>
 __global__ __launch_bounds__(WAVES * kWave)
 void decode_mfma_multi_kernel(MultiArgs m) {
     const int b = (int)blockIdx.x;
     if (b < m.start[1])
-        mfma_group<WAVES, P, RING>(m.g[0], m.nph[0], m.qph[0], b, m.start[1]);
+        mfma_group<WAVES, P, RING, TL>(m.g[0], m.nph[0], m.qph[0], b, m.start[1]);
     else if (b < m.start[2])
-        mfma_group<WAVES, P, RING>(m.g[1], m.nph[1], m.qph[1], b - m.start[1], m.start[2] - m.start[1]);
+        mfma_group<WAVES, P, RING, TL>(m.g[1], m.nph[1], m.qph[1], b - m.start[1], m.start[2] - m.start[1]);
     else if (b < m.start[3])
-        mfma_group<WAVES, P, RING>(m.g[2], m.nph[2], m.qph[2], b - m.start[2], m.start[3] - m.start[2]);
+        mfma_group<WAVES, P, RING, TL>(m.g[2], m.nph[2], m.qph[2], b - m.start[2], m.start[3] - m.start[2]);
     else
-        mfma_group<WAVES, P, RING>(m.g[3], m.nph[3], m.qph[3], b - m.start[3], m.start[4] - m.start[3]);
+        mfma_group<WAVES, P, RING, TL>(m.g[3], m.nph[3], m.qph[3], b - m.start[3], m.start[4] - m.start[3]);
 }
 
 // Static LDS of a kernel as compiled (the partial-sum buffers and the token
@@ -492,14 +494,33 @@ hipError_t launch_decode_groups(const Group *groups, int count, hipStream_t s) {
         if (i < count) start += grid[i];
     }
     m.start[kMaxMulti] = (int)start;
+    // With several token groups every weight tile is read once per group,
+    // by workgroups that sit on one XCD (the grid's width is the budget, a
+    // multiple of 8): ordinary loads let the repeats hit its L2, where
+    // non-temporal ones fetch them again.  Measured per block against
+    // non-temporal loads: a 13B-class block at 32 / 48 tokens 1.3 / 10.4 %
+    // faster, 7B-class at 32 / 64 tokens 1.3 / 1.4 %, 70B-class at 24 / 32
+    // tokens 4.8 / 0.2 %, 2B-style at 96 tokens 3.0-3.7 %; but 2B-style at 33 /
+    // 64 tokens 0.6-2.1 / 0.3-0.7 % slower, so blocks of at most 32 MiB keep
+    // non-temporal loads below 5 token groups.  (Both instances have the same
+    // static LDS: they differ only in the load instruction.)
+    const bool cached = tgroups > 1 && (total > ((int64_t)32 << 20) || tgroups >= 5);
+    const void *k = cached
+                        ? reinterpret_cast<const void *>(
+                              decode_mfma_multi_kernel<kMfWaves, kMfSplit, kMfRing, true>)
+                        : reinterpret_cast<const void *>(kern);
     if (shmem > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)shmem);
+        const hipError_t e =
+            hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)start, (unsigned)tgroups), dim3(kMfThreads),
-                       (size_t)shmem, s, m);
+    if (cached)
+        hipLaunchKernelGGL((decode_mfma_multi_kernel<kMfWaves, kMfSplit, kMfRing, true>),
+                           dim3((unsigned)start, (unsigned)tgroups), dim3(kMfThreads),
+                           (size_t)shmem, s, m);
+    else
+        hipLaunchKernelGGL(kern, dim3((unsigned)start, (unsigned)tgroups), dim3(kMfThreads),
+                           (size_t)shmem, s, m);
     return hipGetLastError();
 }
 

@@ -177,7 +177,9 @@ def test_workload_stream70b_sampled_rows(layer, N):
               seed_rows=layer + N)
 
 
-@pytest.mark.parametrize("N", [33, 64])
+# 24 tokens: two token groups on the matrix-core decode with cached weight
+# loads; 33 and 64: the prefill kernel.
+@pytest.mark.parametrize("N", [24, 33, 64])
 def test_workload_stream70b_many_tokens(N):
     run_layer(W.STREAM70B, 0, N, (bt.BT_I32,), rows_per_proj=64, seed_rows=N)
 
